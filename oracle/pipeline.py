@@ -1,0 +1,98 @@
+"""The whole expert-layer forward and backward, stage by stage.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The forward follows the order the pages imply for a W4A4 expert layer (*Low-Bit
+Precision Training*, section "What W4A4 GEMM Actually Changes"; *miniTE news
+item*, section "Development: Aligning Numerics, Then Making NVFP4 Fast"):
+route, quantise activations, permute tokens by expert, grouped GEMM with gate
+and up projections and SwiGLU, quantise the SwiGLU output, grouped GEMM with
+the down projection, weighted combine back to token order.
+
+The backward computes the two data-gradient and two weight-gradient grouped
+GEMMs of the expert layer with every operand re-quantised to NVFP4 along its
+new contraction dimension (the fully quantised recipe, case (a) of *The
+4-bitter Lesson*, section "Results"), starting from upstream gradients dY2 (of
+the down projection's output rows) and dY13 (of the gate/up output rows).
+
+Storage roundings of the GPU path are mirrored (SwiGLU output stored as BF16,
+expert outputs as FP32), so these functions give an end-to-end oracle result.
+Parity unpinned: after an intermediate tensor is re-quantised, an FP32-vs-FP64
+accumulation difference upstream can move an element across an FP4 rounding
+boundary, so GPU and oracle pipelines agree only statistically; the tests pin
+every stage separately instead, each fed the GPU's own stage inputs.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats as F
+from . import moe
+from . import nvfp4 as Q
+
+
+def gather_rows(t: Q.NVFP4, row_token: np.ndarray) -> Q.NVFP4:
+    """Rows of an NVFP4 tensor in permuted order (codes, scales and the decode
+    scale of each block travel with the row)."""
+    rt = np.asarray(row_token, dtype=np.int64)
+    return Q.NVFP4(t.codes[rt], t.scales[rt], t.G, t.G_block[rt], t.amax)
+
+
+def moe_forward(X: np.ndarray, logits: np.ndarray, W13: np.ndarray, W2: np.ndarray, k: int,
+                renorm: bool = False, out_bf16: bool = False) -> dict:
+    """X [T, H] (FP32 values of BF16 inputs), logits [T, E], W13 [E, 2I, H] with
+    rows [gate_e; up_e], W2 [E, H, I].  Returns every stage's result."""
+    X = np.asarray(X, np.float32)
+    T, H = X.shape
+    E, I2, _ = W13.shape
+    I = I2 // 2
+    ids, w = moe.route_topk(logits, k, renorm)
+    perm = moe.permute(ids, E)
+    Xq = Q.quantize_rows(X, "tensor")
+    Xg = gather_rows(Xq, perm["row_token"])
+    W13q = Q.quantize_rows(np.asarray(W13, np.float32).reshape(E * I2, H), "segment", nseg=E)
+    W2q = Q.quantize_rows(np.asarray(W2, np.float32).reshape(E * H, I), "segment", nseg=E)
+    C1 = moe.grouped_gemm_m(Xg.dequant(), W13q.dequant(), perm["offsets"], E, I2)
+    Hact = moe.swiglu(C1)
+    Hact_bf16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32(Hact)))
+    Hq = Q.quantize_rows(Hact_bf16, "tensor")
+    Y = moe.grouped_gemm_m(Hq.dequant(), W2q.dequant(), perm["offsets"], E, H)
+    Y32 = F.f32(Y)
+    out = moe.combine(Y32, perm["token_row"], w)
+    out = F.f32(out)
+    if out_bf16:
+        out = F.bf16_bits_to_f32(F.f32_to_bf16_bits(out))
+    return dict(topk_ids=ids, topk_w=w, perm=perm, Xq=Xq, Xg=Xg, W13q=W13q, W2q=W2q,
+                C1=C1, Hact=Hact, Hact_bf16=Hact_bf16, Hq=Hq, Y=Y32, out=out)
+
+
+def moe_backward(X: np.ndarray, Hact_bf16: np.ndarray, W13: np.ndarray, W2: np.ndarray,
+                 dY2: np.ndarray, dY13: np.ndarray, perm: dict) -> dict:
+    """Data and weight gradients of both grouped GEMMs, all operands re-quantised
+    along the new contraction dimension.
+
+    dHact  [R, I]     = dY2_e  . W2_e          (contraction over H)
+    dXperm [R, H]     = dY13_e . W13_e         (contraction over 2I)
+    dW2    [E, H, I]  = dY2_e^T  . Hact_e      (contraction over expert e's tokens)
+    dW13   [E, 2I, H] = dY13_e^T . Xperm_e
+    """
+    X = np.asarray(X, np.float32)
+    E, I2, H = W13.shape
+    I = I2 // 2
+    off = perm["offsets"]
+    Xperm = X[np.asarray(perm["row_token"], np.int64)]
+    dY2q = Q.quantize_rows(dY2, "tensor")
+    dY13q = Q.quantize_rows(dY13, "tensor")
+    W2t = Q.quantize_cols_batched(np.asarray(W2, np.float32).reshape(E * H, I), E)      # [E*I, H]
+    W13t = Q.quantize_cols_batched(np.asarray(W13, np.float32).reshape(E * I2, H), E)   # [E*H, 2I]
+    dHact = moe.grouped_gemm_m(dY2q.dequant(), W2t.dequant(), off, E, I)
+    dXperm = moe.grouped_gemm_m(dY13q.dequant(), W13t.dequant(), off, E, H)
+    dY2c, po = Q.quantize_cols(dY2, off)          # [H, Rpad]
+    Hc, _ = Q.quantize_cols(Hact_bf16, off)        # [I, Rpad]
+    dY13c, _ = Q.quantize_cols(dY13, off)         # [2I, Rpad]
+    Xc, _ = Q.quantize_cols(Xperm, off)           # [H, Rpad]
+    dW2 = moe.grouped_gemm_k(dY2c.dequant(), Hc.dequant(), po, E)
+    dW13 = moe.grouped_gemm_k(dY13c.dequant(), Xc.dequant(), po, E)
+    return dict(dY2q=dY2q, dY13q=dY13q, W2t=W2t, W13t=W13t, dHact=dHact, dXperm=dXperm,
+                dY2c=dY2c, Hc=Hc, dY13c=dY13c, Xc=Xc, padded_offsets=po, dW2=dW2, dW13=dW13)
