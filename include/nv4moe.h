@@ -1,0 +1,264 @@
+/*
+ * nv4moe.h -- C ABI of the NVFP4 W4A4 mixture-of-experts expert path for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The path is the expert computation of a mixture-of-experts layer with both
+ * operands of every expert GEMM in NVFP4 ("W4A4"): quantise activations and
+ * weights, permute tokens by expert, run the grouped expert GEMMs (gate/up with
+ * a fused SwiGLU, then down), and combine the top-k expert outputs back into
+ * token order with the routing weights.  Sources:
+ *
+ *   [LBP]  "Low-Bit Precision Training Is Ready for Production: What Engineering
+ *          Leaders Need to Know Before Adopting NVFP4" (vector-labs.ai)
+ *   [4BL]  "The 4-bitter Lesson: Balancing Stability and Performance in NVFP4 RL"
+ *   [MTE]  "miniTE identifies and closes the execution gap in native NVFP4
+ *          reinforcement learning" (n884.com)
+ *
+ * NVFP4 ([4BL], section "Baseline: A starting recipe with stable training
+ * dynamics"): blocks of 16 FP4 E2M1 values, each block with an FP8 E4M3 scale,
+ * plus one FP32 scale for the tensor.  The element and scale formats are those
+ * of the OCP MX v1.0 (E2M1) and OCP OFP8 (E4M3, max 448) specifications.
+ *
+ * Numerics fixed by this library (the pages leave them open; [LBP], section
+ * "The Cross-Engine Alignment Problem", names scale domains, rounding modes,
+ * accumulation precision and operator composition as the choices two engines
+ * must agree on):
+ *   A  = max|x| over the scale group;  S = fp32(2688 / A), or 1 if A == 0 or the
+ *        quotient is not finite;  the stored FP32 tensor scale is G = fp32(1 / S).
+ *   per 16-block:  sf = E4M3_rne_sat(fp32(fp32(max|x_b| / 6) * S));
+ *                  inv = sf ? fp32(S / sf) : 0;   q = E2M1_rne_sat(fp32(x * inv)).
+ *   value(q, sf, G) = e2m1(q) * sf * G.  Element 2i sits in the low nibble of
+ *   byte i; an FP4 code is sign << 3 | magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   Every FP32 step is one correctly rounded operation, so codes and scale bytes
+ *   are exactly defined.  GEMMs multiply the exactly decoded operands
+ *   (e2m1 * sf fits BF16 exactly) with FP32 accumulation and apply G_a * G_b in
+ *   the epilogue.  Every call is deterministic: repeated calls on the same input
+ *   give bitwise identical output.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers unless marked (host).  The caller
+ *     owns every buffer (inputs, outputs, workspace); the library never allocates
+ *     or frees memory and keeps no state besides a thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work; nothing waits on the host and no device value is read back.
+ *   - Shapes are validated on the host before any launch; a failed check returns
+ *     an error status and enqueues nothing.  nv4_last_error() explains it.
+ *   - Faults in the data itself (non-finite values, expert ids out of range, NaN
+ *     logits) are never checked on the host: kernels OR bits into the optional
+ *     device word `dev_status` (NV4_DS_*), which the caller reads after
+ *     synchronising.  Results computed from such data are unspecified.
+ *   - Index arithmetic is 32-bit on the device: rows * K and T * k must stay
+ *     below 2^31.
+ */
+#ifndef NV4MOE_H
+#define NV4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nv4_status {
+  NV4_OK = 0,
+  NV4_EINVAL = -1,        /* NULL where a pointer is required, negative or inconsistent size */
+  NV4_EALIGN = -2,        /* K or a stride not a multiple of 16, or a misaligned pointer */
+  NV4_EUNSUPPORTED = -3,  /* a combination of modes this library does not implement */
+  NV4_EWORKSPACE = -4,    /* workspace smaller than the matching *_workspace() query */
+  NV4_EHIP = -5           /* a HIP launch failed (hipGetLastError) */
+} nv4_status;
+
+typedef enum nv4_dtype { NV4_BF16 = 0, NV4_F32 = 1 } nv4_dtype;
+
+/* quantisation direction (nvfp4_quantize `layout`) */
+#define NV4_ROWS 1          /* blocks of 16 along the contiguous dimension K */
+#define NV4_COLS 2          /* transpose: blocks of 16 down the rows of each segment */
+#define NV4_COLS_BATCHED 3  /* transpose each of nseg equal row-slices separately */
+
+/* tensor-scale grouping (nvfp4_quantize `scale_mode`, nv4_tensor.scale_mode) */
+#define NV4_SCALE_TENSOR 0  /* one G for the whole tensor */
+#define NV4_SCALE_SEGMENT 1 /* one G per segment (expert) */
+#define NV4_SCALE_ROW 2     /* one G per row: the per-token variant */
+
+/* grouped GEMM */
+#define NV4_GROUP_M 0       /* expert e owns rows [offsets[e], offsets[e+1]) of A and C */
+#define NV4_GROUP_K 1       /* expert e owns columns [offsets[e], offsets[e+1]) of the K dimension */
+#define NV4_EPI_NONE 0
+#define NV4_EPI_SWIGLU 1
+
+/* routing flags */
+#define NV4_RENORM 1        /* divide the k routing weights of a token by their sum */
+
+/* dev_status bits */
+#define NV4_DS_NONFINITE 1  /* a quantiser met a NaN or infinity */
+#define NV4_DS_BAD_EXPERT 2 /* an expert id outside [0, E) */
+#define NV4_DS_NAN_LOGIT 4  /* a NaN router logit */
+
+/*
+ * One NVFP4 tensor of logical shape [rows][K] (K % 16 == 0), memory owned by the
+ * caller:
+ *   codes  [rows][K/2]   packed E2M1 codes, row-major, rows K/2 bytes apart
+ *   scales [rows][K/16]  E4M3 block scales, row-major
+ *   tscale               FP32 decode scales G: 1 (SCALE_TENSOR), nseg
+ *                        (SCALE_SEGMENT: segment s = rows [s*rows/nseg, (s+1)*rows/nseg)
+ *                        when used as a grouped-GEMM B operand) or rows (SCALE_ROW)
+ */
+typedef struct nv4_tensor {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tscale;
+  int64_t rows;
+  int64_t K;
+  int32_t scale_mode;
+  int32_t nseg;
+} nv4_tensor;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int nv4_version(void);
+
+/* Text for a status code, and the detail of the last failed call on this thread
+ * (host strings owned by the library; never NULL). */
+const char *nv4_status_string(nv4_status s);
+const char *nv4_last_error(void);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantisation of a BF16 or FP32 matrix.
+ * [4BL] "Baseline: A starting recipe with stable training dynamics" (format);
+ * [4BL] "Why is the NVFP4 pretraining recipe not sufficient for RL?" (one FP32
+ * scale per weight tensor; per-token activation scale, fused into the quantiser);
+ * [4BL] "Improving Gradient Stability", footnote 6 (clip(round(w/s)));
+ * [LBP] "What W4A4 GEMM Actually Changes" (per-tensor or per-token scaling).
+ *
+ *   x, xtype, ldx    input [rows][ldx] (element stride ldx >= K), BF16 or FP32.
+ *   layout           NV4_ROWS: out is [rows][K], blocks along K.
+ *                    NV4_COLS: out is the transpose [K][Kout] of x, where row
+ *                      segment s of x (rows [seg_offsets[s], seg_offsets[s+1]))
+ *                      lands in out columns [seg_padded_offsets[s], ...); every
+ *                      segment starts a new block and is zero-padded to a
+ *                      multiple of 16 (padding is written as code 0 / scale 0).
+ *                      out->K is the column capacity: >= rows + 15 * nseg, % 16.
+ *                      Used for the re-quantised operands of the weight gradients.
+ *                    NV4_COLS_BATCHED: x is nseg equal matrices of rows/nseg rows
+ *                      (rows/nseg % 16 == 0); out is [nseg*K][rows/nseg], matrix s
+ *                      transposed into out rows [s*K, (s+1)*K).  Used for the
+ *                      transposed expert weights of the data gradients.
+ *   scale_mode, nseg NV4_SCALE_TENSOR (nseg ignored unless a segmented layout),
+ *                    NV4_SCALE_SEGMENT (one G per segment; ROWS/COLS_BATCHED use
+ *                    equal segments of rows/nseg rows when seg_offsets is NULL),
+ *                    NV4_SCALE_ROW (ROWS layout only: one G per row, computed in
+ *                    the same single pass).  ngroups = 1, nseg or rows.
+ *   seg_offsets      device int32 [nseg+1], non-decreasing, seg_offsets[nseg] == rows;
+ *                    required for NV4_COLS, optional for SCALE_SEGMENT with ROWS.
+ *   seg_padded_offsets device int32 [nseg+1], required for NV4_COLS: the 16-padded
+ *                    prefix sums (as produced by moe_permute's padded_offsets).
+ *   amax_in          device FP32 [ngroups] or NULL.  When given, the amax pass is
+ *                    skipped and these values are used as A (one pass over x).
+ *   amax_out         device FP32 [ngroups] or NULL: receives the A that was used.
+ *   out              host pointer to a descriptor whose device buffers the caller
+ *                    allocated: codes, scales, tscale (ngroups floats) and the
+ *                    expected output shape in rows/K.  The library sets
+ *                    out->scale_mode and out->nseg.
+ *   ws, ws_bytes     device workspace of at least nvfp4_quantize_workspace().
+ * Errors: EINVAL (NULL pointer, bad sizes, out shape mismatch), EALIGN (K % 16,
+ * ldx % 8 for BF16 / % 4 for FP32, x not 16-byte aligned), EUNSUPPORTED
+ * (SCALE_ROW with a COLS layout), EWORKSPACE, EHIP.
+ */
+size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_mode, int nseg);
+nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                          int layout, int scale_mode, int nseg,
+                          const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                          const float *amax_in, float *amax_out, nv4_tensor *out,
+                          void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * moe_permute -- route tokens to experts and permute them by expert.
+ * [LBP] "What W4A4 GEMM Actually Changes" (expert routing concentrates
+ * activations); [MTE] "Background: Same Weights Did Not Guarantee Same Policy"
+ * (grouped GEMMs over experts).  Router: top-k of the logits (larger first, ties
+ * to the lower expert id); weight = softmax over all E logits at the chosen id
+ * (divided by the k weights' sum with NV4_RENORM).  Permutation: stable counting
+ * sort of the T*k assignments by expert (rows of one expert in increasing token
+ * order), computed without atomics-order dependence.
+ *
+ *   logits           FP32 [T][E] or NULL; NULL means topk_ids (and topk_w) are
+ *                    inputs and only the permutation is computed.
+ *   T, E, k, flags   tokens, experts (1..1024), experts per token (1..min(E, 32)).
+ *   topk_ids, topk_w int32 / FP32 [T][k]: outputs (or inputs when logits NULL;
+ *                    topk_w may then be NULL).
+ *   expert_offsets   int32 [E+1]: exclusive prefix sum of per-expert counts.
+ *   padded_offsets   int32 [E+1] or NULL: same with each count rounded up to 16.
+ *   row_token        int32 [T*k]: token of permuted row r.
+ *   token_row        int32 [T][k]: permuted row of assignment (t, j).
+ *   gather_src, gather_dst  optional (both or neither): NVFP4 tensors [T][K] and
+ *                    [T*k][K]; dst row r = src row row_token[r] (codes and scales;
+ *                    the tensor scale is per tensor and is not copied).
+ *   ws, ws_bytes     device workspace of at least moe_permute_workspace().
+ * Errors: EINVAL, EUNSUPPORTED (E > 1024, k > 32), EWORKSPACE, EHIP.
+ */
+size_t moe_permute_workspace(int64_t T, int E, int k);
+nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
+                       int32_t *topk_ids, float *topk_w,
+                       int32_t *expert_offsets, int32_t *padded_offsets,
+                       int32_t *row_token, int32_t *token_row,
+                       const nv4_tensor *gather_src, nv4_tensor *gather_dst,
+                       void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * nvfp4_grouped_gemm -- one grouped GEMM over experts, C = A_hat . B_hat^T per
+ * expert, both operands NVFP4 (W4A4).  [LBP] "What W4A4 GEMM Actually Changes"
+ * (both operands 4-bit, the GEMM runs on the 4-bit data); [MTE] "Development:
+ * Aligning Numerics, Then Making NVFP4 Fast" (grouped GEMMs); [4BL] "Improving
+ * Gradient Stability" (the product consumes DQ(Q(.)) of the operands).
+ *
+ * NV4_GROUP_M (forward and data gradients):
+ *   A          [M_cap][K] rows grouped by expert: rows [offsets[e], offsets[e+1]).
+ *              A->tscale per tensor or per row.  With a_rows != NULL, GEMM row r
+ *              reads A row a_rows[r] (the permutation gather fused into the load;
+ *              A then holds the un-permuted rows).
+ *   B          [E*Nb][K]; expert e's matrix is rows [e*Nb, (e+1)*Nb); B->tscale per
+ *              tensor or per expert (SCALE_SEGMENT, nseg == E).
+ *              Nb = N (EPI_NONE) or 2N (EPI_SWIGLU: rows [gate_e (N); up_e (N)]).
+ *   C          [M_cap][ldc] of ctype; rows [0, offsets[E]) are written.
+ *   EPI_SWIGLU C = silu(gate) * up with silu(g) = g / (1 + exp(-g)), computed in
+ *              FP32 after the tensor scales; amax_out (device FP32 [1], may be
+ *              NULL) is raised with atomic max to max|C| of the stored values
+ *              (the caller zero-fills it first), ready to feed nvfp4_quantize's
+ *              amax_in.
+ * NV4_GROUP_K (weight gradients):
+ *   A [N][Kcap], B [M][Kcap] with expert e's contraction range
+ *   [offsets[e], offsets[e+1]) (16-aligned, e.g. moe_permute's padded_offsets);
+ *   C [E][N][ldc] (ldc >= M) gets A_e . B_e^T; an empty range gives zeros.
+ *   Tensor scales per tensor.
+ *   offsets    device int32 [E+1].
+ * Errors: EINVAL, EALIGN (K % 16, A->K != B->K), EUNSUPPORTED (SWIGLU with
+ * GROUP_K, row scales with GROUP_K), EWORKSPACE, EHIP.
+ */
+size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K);
+nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
+                              int64_t M_cap, int64_t N, const int32_t *a_rows,
+                              int group_mode, int epilogue,
+                              void *C, nv4_dtype ctype, int64_t ldc, float *amax_out,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- weighted sum of each token's k expert outputs, back in token
+ * order: out[t] = sum_{j=0..k-1} w[t][j] * Y[token_row[t][j]], j ascending, FP32.
+ * [LBP] "What W4A4 GEMM Actually Changes" (expert routing); the weights are the
+ * router weights from moe_permute.
+ *
+ *   Y, ytype, ldy    expert output rows [T*k][ldy] (BF16 or FP32).
+ *   token_row        int32 [T][k] from moe_permute.
+ *   topk_w           FP32 [T][k].
+ *   out, otype       [T][H] (row stride H), BF16 (round to nearest even) or FP32.
+ * Errors: EINVAL, EALIGN (H % 4, ldy % 4), EHIP.
+ */
+nv4_status moe_combine(const void *Y, nv4_dtype ytype, int64_t ldy, const int32_t *token_row,
+                       const float *topk_w, int64_t T, int k, int64_t H,
+                       void *out, nv4_dtype otype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NV4MOE_H */

@@ -1,0 +1,351 @@
+"""Python binding of libnv4moe.so, the NVFP4 W4A4 mixture-of-experts expert path
+for AMD Instinct MI355X (gfx950).
+
+The binding only marshals arguments: torch provides device memory and the
+current HIP stream, every step of the path runs in the library's HIP kernels.
+The entry points carry the names of the C ABI (include/nv4moe.h):
+
+    nvfp4_quantize      NVFP4 quantisation (rows, columns, batched columns)
+    moe_permute         top-k routing and stable permutation by expert (+ row gather)
+    nvfp4_grouped_gemm  grouped NVFP4 x NVFP4 GEMM (GROUP_M with optional SwiGLU, GROUP_K)
+    moe_combine         top-k weighted combine back to token order
+
+``moe_forward`` and ``moe_backward`` compose these calls into the expert layer's
+forward (route, quantise, permute, GEMM + SwiGLU, quantise, GEMM, combine) and
+its four backward grouped GEMMs.  There is no fallback: if the library is not
+built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnv4moe.so")
+
+# constants (mirror include/nv4moe.h)
+NV4_BF16, NV4_F32 = 0, 1
+NV4_ROWS, NV4_COLS, NV4_COLS_BATCHED = 1, 2, 3
+NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT, NV4_SCALE_ROW = 0, 1, 2
+NV4_GROUP_M, NV4_GROUP_K = 0, 1
+NV4_EPI_NONE, NV4_EPI_SWIGLU = 0, 1
+NV4_RENORM = 1
+NV4_DS_NONFINITE, NV4_DS_BAD_EXPERT, NV4_DS_NAN_LOGIT = 1, 2, 4
+STATUS = {0: "NV4_OK", -1: "NV4_EINVAL", -2: "NV4_EALIGN", -3: "NV4_EUNSUPPORTED", -4: "NV4_EWORKSPACE",
+          -5: "NV4_EHIP"}
+
+
+class NV4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class NV4Tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tscale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("scale_mode", ctypes.c_int32),
+                ("nseg", ctypes.c_int32)]
+
+
+_lib = None
+_P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+_SIGS = {
+    "nv4_version": (ctypes.c_int, []),
+    "nv4_status_string": (ctypes.c_char_p, [_I]),
+    "nv4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_quantize_workspace": (_SZ, [_I64, _I64, _I, _I, _I]),
+    "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
+                            _P, _SZ, _P, _P]),
+    "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
+    "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
+                         ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
+    "nvfp4_grouped_gemm_workspace": (_SZ, [_I, _I, _I64, _I64, _I64]),
+    "nvfp4_grouped_gemm": (_I, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _P, _I, _I64, _I64, _P,
+                                _I, _I, _P, _I, _I64, _P, _P, _SZ, _P]),
+    "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I64, _I, _I64, _P, _I, _P]),
+}
+
+
+def load() -> ctypes.CDLL:
+    """Load libnv4moe.so (built in-tree by ``nvfp4_w4a4_moe_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_w4a4_moe_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise NV4Error(status, load().nv4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NV4_BF16
+    if t.dtype == torch.float32:
+        return NV4_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class NVFP4:
+    """Device NVFP4 tensor: codes [rows, K/2] u8, scales [rows, K/16] u8 (E4M3),
+    tscale FP32 decode scales (1, nseg or rows of them)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    rows: int
+    K: int
+    scale_mode: int = NV4_SCALE_TENSOR
+    nseg: int = 1
+
+    @staticmethod
+    def empty(rows: int, K: int, ngroups: int = 1, device="cuda") -> "NVFP4":
+        return NVFP4(torch.empty((rows, K // 2), dtype=torch.uint8, device=device),
+                     torch.empty((rows, K // 16), dtype=torch.uint8, device=device),
+                     torch.empty((max(ngroups, 1),), dtype=torch.float32, device=device), rows, K)
+
+    def c(self) -> NV4Tensor:
+        return NV4Tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(),
+                         self.rows, self.K, self.scale_mode, self.nseg)
+
+
+def _ngroups(rows, scale_mode, nseg):
+    return 1 if scale_mode == NV4_SCALE_TENSOR else (nseg if scale_mode == NV4_SCALE_SEGMENT else rows)
+
+
+def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV4_SCALE_TENSOR, nseg: int = 1,
+                   seg_offsets: torch.Tensor | None = None, seg_padded_offsets: torch.Tensor | None = None,
+                   amax_in: torch.Tensor | None = None, amax_out: torch.Tensor | None = None,
+                   out: NVFP4 | None = None, out_K: int | None = None, ws: torch.Tensor | None = None,
+                   dev_status: torch.Tensor | None = None, stream=None) -> NVFP4:
+    """NVFP4-quantise a 2-D BF16/FP32 tensor (row stride x.stride(0))."""
+    lib = load()
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    if layout == NV4_ROWS:
+        orows, oK = rows, K
+    elif layout == NV4_COLS_BATCHED:
+        orows, oK = nseg * K, rows // nseg
+    else:
+        orows = K
+        oK = out_K if out_K is not None else ((rows + 15 * nseg + 63) // 64) * 64
+    ng = _ngroups(rows, scale_mode, nseg)
+    if out is None:
+        out = NVFP4.empty(orows, oK, ng, device=x.device)
+    if ws is None and amax_out is None and amax_in is None:
+        ws = torch.empty(lib.nvfp4_quantize_workspace(rows, K, layout, scale_mode, nseg), dtype=torch.uint8,
+                         device=x.device)
+    d = out.c()
+    _check(lib.nvfp4_quantize(_ptr(x), _dtype(x), rows, K, x.stride(0), layout, scale_mode, nseg,
+                              _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(amax_in), _ptr(amax_out),
+                              ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), _ptr(dev_status),
+                              _stream(stream)))
+    out.scale_mode, out.nseg = d.scale_mode, d.nseg
+    return out
+
+
+@dataclass
+class Routing:
+    topk_ids: torch.Tensor      # [T, k] int32
+    topk_w: torch.Tensor        # [T, k] fp32
+    offsets: torch.Tensor       # [E+1] int32
+    padded_offsets: torch.Tensor  # [E+1] int32
+    row_token: torch.Tensor     # [T*k] int32
+    token_row: torch.Tensor     # [T, k] int32
+
+
+def moe_permute(logits: torch.Tensor | None, E: int, k: int, T: int | None = None, flags: int = 0,
+                topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                gather_src: NVFP4 | None = None, gather_dst: NVFP4 | None = None,
+                ws: torch.Tensor | None = None, dev_status: torch.Tensor | None = None,
+                stream=None, device="cuda") -> Routing:
+    lib = load()
+    if logits is not None:
+        assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.shape[1] == E
+        T = logits.shape[0]
+        device = logits.device
+    elif topk_ids is not None:
+        T = topk_ids.shape[0]
+        device = topk_ids.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
+    if topk_w is None and logits is not None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+    padded = torch.empty((E + 1,), dtype=torch.int32, device=device)
+    row_token = torch.empty((T * k,), dtype=torch.int32, device=device)
+    token_row = torch.empty((T, k), dtype=torch.int32, device=device)
+    if ws is None:
+        ws = torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device)
+    gs = ctypes.byref(gather_src.c()) if gather_src is not None else None
+    gd = ctypes.byref(gather_dst.c()) if gather_dst is not None else None
+    _check(lib.moe_permute(_ptr(logits), T, E, k, flags, _ptr(topk_ids), _ptr(topk_w), _ptr(offsets),
+                           _ptr(padded), _ptr(row_token), _ptr(token_row), gs, gd, _ptr(ws), ws.numel(),
+                           _ptr(dev_status), _stream(stream)))
+    return Routing(topk_ids, topk_w, offsets, padded, row_token, token_row)
+
+
+def nvfp4_grouped_gemm(A: NVFP4, B: NVFP4, offsets: torch.Tensor, E: int, N: int, M_cap: int | None = None,
+                       a_rows: torch.Tensor | None = None, group_mode: int = NV4_GROUP_M,
+                       epilogue: int = NV4_EPI_NONE, out_dtype=torch.float32, C: torch.Tensor | None = None,
+                       amax_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """GROUP_M: C [M_cap, N] = per-expert A_e . B_e^T (SwiGLU: N output columns from 2N
+    rows of B per expert).  GROUP_K: C [E, N=A.rows, M=B.rows] over per-expert K ranges."""
+    lib = load()
+    if group_mode == NV4_GROUP_M:
+        if M_cap is None:
+            M_cap = A.rows
+        if C is None:
+            C = torch.empty((M_cap, N), dtype=out_dtype, device=A.codes.device)
+        ldc = C.stride(0)
+    else:
+        N = A.rows
+        if C is None:
+            C = torch.empty((E, A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
+        ldc = C.stride(1)
+        M_cap = 0
+    a, b = A.c(), B.c()
+    _check(lib.nvfp4_grouped_gemm(ctypes.byref(a), ctypes.byref(b), _ptr(offsets), E, M_cap, N, _ptr(a_rows),
+                                  group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out), None, 0,
+                                  _stream(stream)))
+    return C
+
+
+def moe_combine(Y: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor, out_dtype=torch.float32,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    lib = load()
+    T, k = token_row.shape
+    H = Y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=Y.device)
+    _check(lib.moe_combine(_ptr(Y), _dtype(Y), Y.stride(0), _ptr(token_row), _ptr(topk_w), T, k, H, _ptr(out),
+                           _dtype(out), _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------------------- layer composition
+
+@dataclass
+class ExpertWeights:
+    """Quantised expert weights: W13 [E*2I, H] (rows gate_e then up_e) and W2 [E*H, I],
+    one tensor scale per expert and projection."""
+    w13: NVFP4
+    w2: NVFP4
+    E: int
+    H: int
+    I: int
+
+
+def quantize_expert_weights(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> ExpertWeights:
+    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> NVFP4 with per-expert scales."""
+    E, I2, H = W13.shape
+    w13 = nvfp4_quantize(W13.reshape(E * I2, H), scale_mode=NV4_SCALE_SEGMENT, nseg=E, stream=stream)
+    w2 = nvfp4_quantize(W2.reshape(E * H, I2 // 2), scale_mode=NV4_SCALE_SEGMENT, nseg=E, stream=stream)
+    return ExpertWeights(w13, w2, E, H, I2 // 2)
+
+
+@dataclass
+class ForwardBuffers:
+    """Every intermediate of one forward, preallocated so that a timed forward
+    enqueues kernels only."""
+    xq: NVFP4
+    xg: NVFP4
+    hact: torch.Tensor
+    hamax: torch.Tensor
+    hq: NVFP4
+    y: torch.Tensor
+    out: torch.Tensor
+    qws: torch.Tensor
+    pws: torch.Tensor
+    hq_ws: torch.Tensor
+    routing: Routing | None = None
+
+
+def alloc_forward(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat16, hact_dtype=torch.bfloat16,
+                  device="cuda") -> ForwardBuffers:
+    lib = load()
+    R = T * k
+    return ForwardBuffers(
+        xq=NVFP4.empty(T, H, 1, device), xg=NVFP4.empty(R, H, 1, device),
+        hact=torch.empty((R, I), dtype=hact_dtype, device=device),
+        hamax=torch.zeros((1,), dtype=torch.float32, device=device),
+        hq=NVFP4.empty(R, I, 1, device),
+        y=torch.empty((R, H), dtype=torch.float32, device=device),
+        out=torch.empty((T, H), dtype=out_dtype, device=device),
+        qws=torch.empty(lib.nvfp4_quantize_workspace(T, H, NV4_ROWS, NV4_SCALE_TENSOR, 1), dtype=torch.uint8,
+                        device=device),
+        pws=torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device),
+        hq_ws=torch.empty(256, dtype=torch.uint8, device=device))
+
+
+class _Stage:
+    """Optional per-stage timing: HIP events recorded on the launch stream."""
+
+    def __init__(self, events, name, stream):
+        self.events, self.name, self.stream = events, name, stream
+
+    def __enter__(self):
+        if self.events is not None:
+            self.t0 = torch.cuda.Event(enable_timing=True)
+            self.t0.record(self.stream)
+
+    def __exit__(self, *exc):
+        if self.events is not None:
+            t1 = torch.cuda.Event(enable_timing=True)
+            t1.record(self.stream)
+            self.events.append((self.name, self.t0, t1))
+
+
+def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int, bufs: ForwardBuffers | None = None,
+                fuse_gather: bool = True, stream=None, stage_events: list | None = None) -> ForwardBuffers:
+    """One expert-layer forward on device: returns the buffers (out holds the result).
+    With stage_events (a list), (name, start_event, end_event) is appended per stage."""
+    T, H = x.shape
+    if bufs is None:
+        bufs = alloc_forward(T, H, w.E, k, w.I, device=x.device)
+    R = T * k
+    st = stream if stream is not None else torch.cuda.current_stream()
+    with _Stage(stage_events, "quantize_x", st):
+        nvfp4_quantize(x, out=bufs.xq, ws=bufs.qws, stream=stream)
+    with _Stage(stage_events, "route_permute", st):
+        if fuse_gather:
+            bufs.routing = moe_permute(logits, w.E, k, ws=bufs.pws, stream=stream)
+            a, a_rows = bufs.xq, bufs.routing.row_token
+        else:
+            bufs.routing = moe_permute(logits, w.E, k, gather_src=bufs.xq, gather_dst=bufs.xg, ws=bufs.pws,
+                                       stream=stream)
+            bufs.xg.tscale = bufs.xq.tscale
+            a, a_rows = bufs.xg, None
+    with _Stage(stage_events, "gemm1_swiglu", st):
+        bufs.hamax.zero_()
+        nvfp4_grouped_gemm(a, w.w13, bufs.routing.offsets, w.E, w.I, M_cap=R, a_rows=a_rows,
+                           epilogue=NV4_EPI_SWIGLU, C=bufs.hact, amax_out=bufs.hamax, stream=stream)
+    with _Stage(stage_events, "quantize_hact", st):
+        nvfp4_quantize(bufs.hact, amax_in=bufs.hamax, out=bufs.hq, stream=stream)
+    with _Stage(stage_events, "gemm2", st):
+        nvfp4_grouped_gemm(bufs.hq, w.w2, bufs.routing.offsets, w.E, H, M_cap=R, C=bufs.y, stream=stream)
+    with _Stage(stage_events, "combine", st):
+        moe_combine(bufs.y, bufs.routing.token_row, bufs.routing.topk_w, out=bufs.out, stream=stream)
+    return bufs

@@ -1,0 +1,348 @@
+// C ABI of the NVFP4 W4A4 expert path (declarations and contracts: include/nv4moe.h).
+// Host side only: argument validation, workspace carving, dispatch to the kernel
+// launchers, and mapping of HIP errors.  No call allocates memory or waits on the
+// device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "../../include/nv4moe.h"
+#include "nv4_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+nv4_status fail(nv4_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+nv4_status ok() {
+  snprintf(g_err, sizeof(g_err), "no error");
+  return NV4_OK;
+}
+
+nv4_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(NV4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int ngroups_of(int64_t rows, int scale_mode, int nseg) {
+  if (scale_mode == NV4_SCALE_TENSOR) return 1;
+  if (scale_mode == NV4_SCALE_SEGMENT) return nseg;
+  return (int)rows;
+}
+
+}  // namespace
+
+namespace nv4 {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace nv4
+
+extern "C" {
+
+int nv4_version(void) { return 100; }
+
+const char *nv4_status_string(nv4_status s) {
+  switch (s) {
+    case NV4_OK: return "ok";
+    case NV4_EINVAL: return "invalid argument";
+    case NV4_EALIGN: return "misaligned size or pointer";
+    case NV4_EUNSUPPORTED: return "unsupported mode combination";
+    case NV4_EWORKSPACE: return "workspace too small";
+    case NV4_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *nv4_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------- quantisation
+
+size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_mode, int nseg) {
+  (void)K;
+  (void)layout;
+  const int ng = ngroups_of(rows, scale_mode, nseg);
+  return round256((size_t)std::max(ng, 1) * sizeof(float));
+}
+
+nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                          int layout, int scale_mode, int nseg,
+                          const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                          const float *amax_in, float *amax_out, nv4_tensor *out,
+                          void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  if (!out) return fail(NV4_EINVAL, "nvfp4_quantize: out descriptor is NULL");
+  if (rows < 0 || K < 0) return fail(NV4_EINVAL, "nvfp4_quantize: negative shape");
+  if (xtype != NV4_BF16 && xtype != NV4_F32) return fail(NV4_EINVAL, "nvfp4_quantize: bad input dtype");
+  if (layout != NV4_ROWS && layout != NV4_COLS && layout != NV4_COLS_BATCHED)
+    return fail(NV4_EINVAL, "nvfp4_quantize: bad layout %d", layout);
+  if (scale_mode != NV4_SCALE_TENSOR && scale_mode != NV4_SCALE_SEGMENT && scale_mode != NV4_SCALE_ROW)
+    return fail(NV4_EINVAL, "nvfp4_quantize: bad scale_mode %d", scale_mode);
+  if (scale_mode == NV4_SCALE_ROW && layout != NV4_ROWS)
+    return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: per-row scales need the NV4_ROWS layout");
+  if (K % 16) return fail(NV4_EALIGN, "nvfp4_quantize: K = %lld is not a multiple of 16", (long long)K);
+  if (ldx < K) return fail(NV4_EINVAL, "nvfp4_quantize: ldx < K");
+  const int64_t esz = xtype == NV4_F32 ? 4 : 2;
+  if ((ldx * esz) % 16 || !aligned(x, 16))
+    return fail(NV4_EALIGN, "nvfp4_quantize: x and its row stride must be 16-byte aligned");
+  const bool seg_layout = layout != NV4_ROWS;
+  if ((scale_mode == NV4_SCALE_SEGMENT || seg_layout) && nseg <= 0)
+    return fail(NV4_EINVAL, "nvfp4_quantize: nseg must be positive");
+  if (layout == NV4_COLS && (!seg_offsets || !seg_padded_offsets))
+    return fail(NV4_EINVAL, "nvfp4_quantize: NV4_COLS needs seg_offsets and seg_padded_offsets");
+  if (layout == NV4_COLS_BATCHED && (rows % nseg || (rows / nseg) % 16))
+    return fail(NV4_EALIGN, "nvfp4_quantize: NV4_COLS_BATCHED needs rows/nseg to be a multiple of 16");
+  if ((layout == NV4_ROWS || layout == NV4_COLS_BATCHED) && scale_mode == NV4_SCALE_SEGMENT && !seg_offsets &&
+      rows % nseg)
+    return fail(NV4_EINVAL, "nvfp4_quantize: equal segments need rows %% nseg == 0");
+  if (layout == NV4_COLS && scale_mode == NV4_SCALE_SEGMENT && !seg_offsets)
+    return fail(NV4_EINVAL, "nvfp4_quantize: segment scales need seg_offsets");
+  if (rows >= (1ll << 31) || K >= (1ll << 31)) return fail(NV4_EINVAL, "nvfp4_quantize: shape too large");
+  int64_t out_rows, out_K;
+  if (layout == NV4_ROWS) { out_rows = rows; out_K = K; }
+  else if (layout == NV4_COLS_BATCHED) { out_rows = (int64_t)nseg * K; out_K = rows / nseg; }
+  else { out_rows = K; out_K = out->K; }
+  if (out->rows != out_rows) return fail(NV4_EINVAL, "nvfp4_quantize: out->rows = %lld, expected %lld",
+                                         (long long)out->rows, (long long)out_rows);
+  if (layout == NV4_COLS) {
+    if (out->K % 64) return fail(NV4_EALIGN, "nvfp4_quantize: NV4_COLS needs out->K %% 64 == 0");
+    if (out->K < rows + 15 * (int64_t)nseg)
+      return fail(NV4_EINVAL, "nvfp4_quantize: out->K must be >= rows + 15 * nseg (padded capacity)");
+  } else if (out->K != out_K) {
+    return fail(NV4_EINVAL, "nvfp4_quantize: out->K = %lld, expected %lld", (long long)out->K, (long long)out_K);
+  }
+  if (out_rows * out_K >= (1ll << 32)) return fail(NV4_EINVAL, "nvfp4_quantize: output too large");
+  if ((rows > 0 && K > 0) && (!x || !out->codes || !out->scales))
+    return fail(NV4_EINVAL, "nvfp4_quantize: NULL data pointer");
+  if (!out->tscale) return fail(NV4_EINVAL, "nvfp4_quantize: out->tscale is NULL");
+  if (!aligned(out->codes, 16) || !aligned(out->scales, 4))
+    return fail(NV4_EALIGN, "nvfp4_quantize: codes must be 16-byte and scales 4-byte aligned");
+  const int ng = ngroups_of(rows, scale_mode, nseg);
+  const size_t need = nvfp4_quantize_workspace(rows, K, layout, scale_mode, nseg);
+  if (!amax_out && !amax_in && (!ws || ws_bytes < need))
+    return fail(NV4_EWORKSPACE, "nvfp4_quantize: workspace of %zu bytes required", need);
+
+  out->scale_mode = scale_mode;
+  out->nseg = scale_mode == NV4_SCALE_SEGMENT ? nseg : (scale_mode == NV4_SCALE_ROW ? (int32_t)rows : 1);
+  if (rows == 0 || K == 0) {
+    if (ng == 0) return ok();
+  }
+  nv4::QuantArgs a{};
+  a.x = x;
+  a.x_is_f32 = xtype == NV4_F32;
+  a.rows = rows;
+  a.K = K;
+  a.ldx = ldx;
+  a.layout = layout;
+  a.scale_mode = scale_mode;
+  a.nseg = nseg > 0 ? nseg : 1;
+  a.seg_offsets = seg_offsets;
+  a.seg_padded_offsets = seg_padded_offsets;
+  a.amax_in = amax_in;
+  a.amax_acc = amax_out ? amax_out : static_cast<float *>(ws);
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.tscale = out->tscale;
+  a.out_rows = out_rows;
+  a.out_K = layout == NV4_COLS ? out->K : out_K;
+  a.dev_status = dev_status;
+  a.ngroups = ng;
+  return from_hip(nv4::launch_quantize(a, static_cast<hipStream_t>(stream)), "nvfp4_quantize");
+}
+
+// ---------------------------------------------------------------- routing / permutation
+
+size_t moe_permute_workspace(int64_t T, int E, int k) {
+  if (T < 0 || E <= 0 || k <= 0) return 0;
+  return nv4::permute_workspace_bytes(T, E, k);
+}
+
+nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
+                       int32_t *topk_ids, float *topk_w,
+                       int32_t *expert_offsets, int32_t *padded_offsets,
+                       int32_t *row_token, int32_t *token_row,
+                       const nv4_tensor *gather_src, nv4_tensor *gather_dst,
+                       void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  if (T < 0) return fail(NV4_EINVAL, "moe_permute: T < 0");
+  if (E <= 0 || k <= 0) return fail(NV4_EINVAL, "moe_permute: E and k must be positive");
+  if (E > 1024) return fail(NV4_EUNSUPPORTED, "moe_permute: E = %d exceeds 1024", E);
+  if (k > 32 || k > E) return fail(NV4_EUNSUPPORTED, "moe_permute: k = %d must be <= min(E, 32)", k);
+  if (T * (int64_t)k >= (1ll << 31)) return fail(NV4_EINVAL, "moe_permute: T * k must stay below 2^31");
+  if (flags & ~NV4_RENORM) return fail(NV4_EINVAL, "moe_permute: unknown flags");
+  if (!topk_ids || !expert_offsets || !row_token || !token_row)
+    return fail(NV4_EINVAL, "moe_permute: NULL output pointer");
+  if (logits && !topk_w) return fail(NV4_EINVAL, "moe_permute: topk_w is required with logits");
+  if ((gather_src == nullptr) != (gather_dst == nullptr))
+    return fail(NV4_EINVAL, "moe_permute: gather needs both src and dst");
+  int64_t gK = 0;
+  if (gather_src) {
+    if (gather_src->K != gather_dst->K || gather_src->K % 16 || gather_src->K <= 0)
+      return fail(NV4_EALIGN, "moe_permute: gather tensors need equal K, multiple of 16");
+    if (gather_src->rows != T || gather_dst->rows != T * (int64_t)k)
+      return fail(NV4_EINVAL, "moe_permute: gather shapes must be [T][K] -> [T*k][K]");
+    if (!gather_src->codes || !gather_src->scales || !gather_dst->codes || !gather_dst->scales)
+      return fail(NV4_EINVAL, "moe_permute: NULL gather buffer");
+    if (!aligned(gather_src->codes, 16) || !aligned(gather_dst->codes, 16) || !aligned(gather_src->scales, 4) ||
+        !aligned(gather_dst->scales, 4))
+      return fail(NV4_EALIGN, "moe_permute: gather buffers misaligned");
+    gK = gather_src->K;
+  }
+  const size_t need = nv4::permute_workspace_bytes(T, E, k);
+  if (!ws || ws_bytes < need) return fail(NV4_EWORKSPACE, "moe_permute: workspace of %zu bytes required", need);
+  nv4::PermuteArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.flags = flags;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.expert_offsets = expert_offsets;
+  a.padded_offsets = padded_offsets;
+  a.row_token = row_token;
+  a.token_row = token_row;
+  if (gather_src) {
+    a.src_codes = gather_src->codes;
+    a.src_scales = gather_src->scales;
+    a.dst_codes = gather_dst->codes;
+    a.dst_scales = gather_dst->scales;
+  }
+  a.gather_K = gK;
+  const int64_t R = T * k;
+  const int64_t nchunks = std::max<int64_t>(1, (R + nv4::kPermuteChunk - 1) / nv4::kPermuteChunk);
+  a.chunk_counts = static_cast<int32_t *>(ws);
+  a.local_rank = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + round256((size_t)nchunks * E * 4));
+  a.dev_status = dev_status;
+  return from_hip(nv4::launch_permute(a, static_cast<hipStream_t>(stream)), "moe_permute");
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+
+size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K) {
+  (void)group_mode; (void)E; (void)M_cap; (void)N; (void)K;
+  return 0;
+}
+
+nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
+                              int64_t M_cap, int64_t N, const int32_t *a_rows,
+                              int group_mode, int epilogue,
+                              void *C, nv4_dtype ctype, int64_t ldc, float *amax_out,
+                              void *ws, size_t ws_bytes, void *stream) {
+  (void)ws; (void)ws_bytes;
+  if (!A || !B || !offsets || !C) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: NULL argument");
+  if (E <= 0 || E > 1024) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: E must be in [1, 1024]");
+  if (group_mode != NV4_GROUP_M && group_mode != NV4_GROUP_K)
+    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: bad group_mode");
+  if (epilogue != NV4_EPI_NONE && epilogue != NV4_EPI_SWIGLU)
+    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: bad epilogue");
+  if (ctype != NV4_BF16 && ctype != NV4_F32) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: bad C dtype");
+  if (A->K != B->K) return fail(NV4_EALIGN, "nvfp4_grouped_gemm: A->K != B->K");
+  if (A->K <= 0 || A->K % 64)
+    return fail(NV4_EALIGN, "nvfp4_grouped_gemm: K = %lld must be a positive multiple of 64", (long long)A->K);
+  if (!A->codes || !A->scales || !A->tscale || !B->codes || !B->scales || !B->tscale)
+    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: NULL tensor buffer");
+  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4))
+    return fail(NV4_EALIGN, "nvfp4_grouped_gemm: codes must be 16-byte and scales 4-byte aligned");
+  if (A->rows * (A->K / 2) >= (1ll << 40) || B->rows * (B->K / 2) >= (1ll << 40))
+    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: operand too large");
+  nv4::GemmArgs g{};
+  g.a_codes = A->codes;
+  g.a_scales = A->scales;
+  g.a_tscale = A->tscale;
+  g.a_scale_mode = A->scale_mode;
+  g.a_rows = A->rows;
+  g.K = A->K;
+  g.a_rows_index = a_rows;
+  g.b_codes = B->codes;
+  g.b_scales = B->scales;
+  g.b_tscale = B->tscale;
+  g.b_scale_mode = B->scale_mode;
+  g.b_rows = B->rows;
+  g.offsets = offsets;
+  g.E = E;
+  g.M_cap = M_cap;
+  g.N = N;
+  g.group_mode = group_mode;
+  g.epilogue = epilogue;
+  g.C = C;
+  g.c_is_f32 = ctype == NV4_F32;
+  g.ldc = ldc;
+  g.amax_out = amax_out;
+  if (group_mode == NV4_GROUP_M) {
+    const int64_t Nb = epilogue == NV4_EPI_SWIGLU ? 2 * N : N;
+    if (N <= 0) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: N must be positive");
+    if (B->rows != (int64_t)E * Nb)
+      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B->rows = %lld, expected E * %lld", (long long)B->rows,
+                  (long long)Nb);
+    if (A->scale_mode == NV4_SCALE_SEGMENT)
+      return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: A scales must be per tensor or per row");
+    if (B->scale_mode == NV4_SCALE_ROW)
+      return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: B scales must be per tensor or per expert");
+    if (B->scale_mode == NV4_SCALE_SEGMENT && B->nseg != E)
+      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B has %d scale segments, expected E = %d", B->nseg, E);
+    if (M_cap < 0 || (a_rows == nullptr && M_cap > A->rows))
+      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: M_cap exceeds the rows of A");
+    if (ldc < N) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: ldc < N");
+    if (M_cap >= (1ll << 31)) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: M_cap must stay below 2^31");
+  } else {
+    if (epilogue != NV4_EPI_NONE) return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K has no SwiGLU epilogue");
+    if (a_rows) return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K takes no row index");
+    if (A->scale_mode != NV4_SCALE_TENSOR || B->scale_mode != NV4_SCALE_TENSOR)
+      return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K needs per-tensor scales");
+    if (ldc < B->rows) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: ldc < rows of B");
+    g.N = B->rows;
+  }
+  return from_hip(nv4::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)), "nvfp4_grouped_gemm");
+}
+
+// ---------------------------------------------------------------- combine
+
+nv4_status moe_combine(const void *Y, nv4_dtype ytype, int64_t ldy, const int32_t *token_row,
+                       const float *topk_w, int64_t T, int k, int64_t H,
+                       void *out, nv4_dtype otype, void *stream) {
+  if (T < 0 || k <= 0 || H <= 0) return fail(NV4_EINVAL, "moe_combine: bad shape");
+  if (ytype != NV4_BF16 && ytype != NV4_F32) return fail(NV4_EINVAL, "moe_combine: bad Y dtype");
+  if (otype != NV4_BF16 && otype != NV4_F32) return fail(NV4_EINVAL, "moe_combine: bad out dtype");
+  if (T > 0 && (!Y || !token_row || !topk_w || !out)) return fail(NV4_EINVAL, "moe_combine: NULL pointer");
+  if (H % 4 || ldy % 4 || ldy < H) return fail(NV4_EALIGN, "moe_combine: H and ldy must be multiples of 4, ldy >= H");
+  if (!aligned(Y, 16) || !aligned(out, 16)) return fail(NV4_EALIGN, "moe_combine: Y and out must be 16-byte aligned");
+  nv4::CombineArgs a{};
+  a.Y = Y;
+  a.y_is_f32 = ytype == NV4_F32;
+  a.ldy = ldy;
+  a.token_row = token_row;
+  a.topk_w = topk_w;
+  a.T = T;
+  a.k = k;
+  a.H = H;
+  a.out = out;
+  a.out_is_f32 = otype == NV4_F32;
+  return from_hip(nv4::launch_combine(a, static_cast<hipStream_t>(stream)), "moe_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Top-k weighted combine for gfx950: out[t] = sum_{j=0..k-1} w[t][j] * Y[token_row[t][j]],
+// accumulated in FP32 in ascending j (one fused multiply-add per term), stored
+// as FP32 or BF16 (round to nearest even).  The weights are the router weights
+// ("Low-Bit Precision Training ...", section "What W4A4 GEMM Actually Changes":
+// expert routing); the rows come from the down-projection grouped GEMM.
+//
+// Memory bound: each token reads k rows of H values and writes one row.  One
+// workgroup per token; every thread owns 4 consecutive columns (16-byte loads of
+// FP32 rows, 8-byte loads of BF16 rows); the k row indices and weights are
+// wave-uniform scalar loads.
+#include "nv4_device.h"
+#include "nv4_internal.h"
+
+namespace nv4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool Y_F32, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
+  const int64_t t = blockIdx.x;
+  const int32_t *tr = a.token_row + t * a.k;
+  const float *tw = a.topk_w + t * a.k;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < a.H; c += kThreads * 4) {
+    float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int64_t r = tr[j];
+      const float w = tw[j];
+      float y0, y1, y2, y3;
+      if (Y_F32) {
+        const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.Y) + r * a.ldy + c);
+        y0 = v.x; y1 = v.y; y2 = v.z; y3 = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.Y) + r * a.ldy + c);
+        y0 = __uint_as_float(v.x << 16); y1 = __uint_as_float(v.x & 0xFFFF0000u);
+        y2 = __uint_as_float(v.y << 16); y3 = __uint_as_float(v.y & 0xFFFF0000u);
+      }
+      acc0 = __builtin_fmaf(w, y0, acc0);
+      acc1 = __builtin_fmaf(w, y1, acc1);
+      acc2 = __builtin_fmaf(w, y2, acc2);
+      acc3 = __builtin_fmaf(w, y3, acc3);
+    }
+    if (OUT_F32) {
+      *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + t * a.H + c) = make_float4(acc0, acc1, acc2, acc3);
+    } else {
+      const uint32_t lo = f32_to_bf16_rne(acc0) | (f32_to_bf16_rne(acc1) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc2) | (f32_to_bf16_rne(acc3) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + t * a.H + c) = make_uint2(lo, hi);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  const unsigned grid = (unsigned)a.T;
+  if (a.y_is_f32) {
+    if (a.out_is_f32) k_combine<true, true><<<grid, kThreads, 0, stream>>>(a);
+    else k_combine<true, false><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+    if (a.out_is_f32) k_combine<false, true><<<grid, kThreads, 0, stream>>>(a);
+    else k_combine<false, false><<<grid, kThreads, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nv4

@@ -1,0 +1,91 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+// Every launcher only enqueues work on `stream`; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nv4 {
+
+// ---------------------------------------------------------------- quantisation
+struct QuantArgs {
+  const void *x;
+  int x_is_f32;
+  int64_t rows, K, ldx;
+  int layout;        // NV4_ROWS / NV4_COLS / NV4_COLS_BATCHED
+  int scale_mode;    // NV4_SCALE_*
+  int nseg;
+  const int32_t *seg_offsets;         // may be null
+  const int32_t *seg_padded_offsets;  // NV4_COLS
+  const float *amax_in;               // may be null
+  float *amax_acc;                    // ngroups floats: amax_out or workspace
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tscale;
+  int64_t out_rows, out_K;            // output tensor shape (codes row stride out_K/2)
+  int32_t *dev_status;
+  int ngroups;
+};
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- routing / permutation
+constexpr int kPermuteChunk = 1024;  // assignments ranked per wave
+struct PermuteArgs {
+  const float *logits;
+  int64_t T;
+  int E, k, flags;
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *expert_offsets, *padded_offsets, *row_token, *token_row;
+  const uint8_t *src_codes, *src_scales;
+  uint8_t *dst_codes, *dst_scales;
+  int64_t gather_K;  // 0 = no gather
+  int32_t *chunk_counts;  // workspace [nchunks][E]
+  int32_t *local_rank;    // workspace [T*k]
+  int32_t *dev_status;
+};
+size_t permute_workspace_bytes(int64_t T, int E, int k);
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- grouped GEMM
+struct GemmArgs {
+  const uint8_t *a_codes, *a_scales;
+  const float *a_tscale;
+  int a_scale_mode;
+  int64_t a_rows, K;
+  const int32_t *a_rows_index;   // may be null
+  const uint8_t *b_codes, *b_scales;
+  const float *b_tscale;
+  int b_scale_mode;
+  int64_t b_rows;
+  const int32_t *offsets;
+  int E;
+  int64_t M_cap, N;              // N = output columns
+  int group_mode, epilogue;
+  void *C;
+  int c_is_f32;
+  int64_t ldc;
+  float *amax_out;
+};
+hipError_t launch_grouped_gemm(const GemmArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- combine
+struct CombineArgs {
+  const void *Y;
+  int y_is_f32;
+  int64_t ldy;
+  const int32_t *token_row;
+  const float *topk_w;
+  int64_t T;
+  int k;
+  int64_t H;
+  void *out;
+  int out_is_f32;
+};
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+// number of compute units of the current device (cached per device)
+int device_cu_count();
+
+}  // namespace nv4

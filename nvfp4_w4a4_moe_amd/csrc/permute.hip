@@ -1,0 +1,232 @@
+// Routing and permutation by expert for gfx950.
+//
+// "Low-Bit Precision Training ...", section "What W4A4 GEMM Actually Changes":
+// expert routing concentrates activations on the chosen experts; "miniTE ...",
+// section "Background: Same Weights Did Not Guarantee Same Policy": the expert
+// work runs as grouped GEMMs, which need the routed rows of each expert to be
+// contiguous.
+//
+// Router: top-k of the logits, larger first, ties to the lower expert id; the
+// weight of a chosen expert is its softmax probability over all E logits (FP32,
+// fixed-order reductions).  Permutation: a stable counting sort of the flat
+// assignments f = t*k + j by expert, so the rows of one expert are in increasing
+// (t, j) order.  The rank of every assignment is computed without atomics:
+//   1. one wave per chunk of kPermuteChunk assignments ranks each assignment
+//      among equal experts inside the chunk (wave ballots over the id bits,
+//      chunk-local counters in LDS), and writes the chunk's expert histogram;
+//   2. one workgroup turns the histograms into per-(chunk, expert) bases and the
+//      expert offsets (exclusive prefix sums);
+//   3. every assignment's row is base + local rank; a scatter writes the maps.
+// The result is one exactly defined permutation, identical on every run.
+#include <algorithm>
+
+#include "nv4_device.h"
+#include "nv4_internal.h"
+#include "../../include/nv4moe.h"
+
+namespace nv4 {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / kWave;
+
+// one wave per token: softmax statistics, then k rounds of a wave-wide argmax
+__global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int E = a.E;
+  const float *lg = a.logits + t * E;
+  float lv[kMaxPerLane];
+  float mx = -INFINITY;
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    lv[i] = -INFINITY;
+    if (e < E) {
+      lv[i] = lg[e];
+      nan |= lv[i] != lv[i];
+      mx = fmaxf(mx, lv[i]);
+    }
+  }
+  mx = wave_max(mx);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) s += expf(lv[i] - mx);
+  }
+  s = wave_sum(s);
+  uint32_t taken = 0;
+  int my_id = 0;
+  float my_w = 0.0f, wsum = 0.0f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (lv[i] == bv && e < bi))) { bv = lv[i]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float w = expf(bv - mx) / s;
+    wsum += w;
+    if (lane == j) { my_id = bi; my_w = w; }
+  }
+  if (a.flags & NV4_RENORM) my_w = my_w / wsum;
+  if (lane < a.k) {
+    a.topk_ids[t * a.k + lane] = my_id;
+    a.topk_w[t * a.k + lane] = my_w;
+  }
+  if (nan && lane == 0 && a.dev_status) atomicOr(a.dev_status, kDsNanLogit);
+}
+
+// one wave per chunk: rank of each assignment among the chunk's assignments to
+// the same expert (in flat order), and the chunk's expert histogram
+__global__ __launch_bounds__(64) void k_rank(PermuteArgs a, int nbits) {
+  __shared__ int cnt[kMaxE];
+  const int lane = threadIdx.x;
+  const int E = a.E;
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __syncthreads();
+  const int64_t R = a.T * a.k;
+  const int64_t f0 = (int64_t)blockIdx.x * kPermuteChunk;
+  const int64_t f1 = std::min<int64_t>(f0 + kPermuteChunk, R);
+  bool badid = false;
+  for (int64_t fb = f0; fb < f1; fb += kWave) {
+    const int64_t f = fb + lane;
+    const bool act = f < f1;
+    int e = act ? a.topk_ids[f] : 0;
+    if (e < 0 || e >= E) { badid |= act; e = 0; }
+    uint64_t match = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(match & below);
+    const int base = cnt[e];
+    __syncthreads();
+    if (act) {
+      a.local_rank[f] = base + rank;
+      if ((match >> lane) == 1ull) cnt[e] = base + __popcll(match);  // highest lane of its group
+    }
+    __syncthreads();
+  }
+  for (int e = lane; e < E; e += kWave) a.chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+  if (badid && a.dev_status) atomicOr(a.dev_status, kDsBadExpert);
+}
+
+// one workgroup: chunk histograms -> per-(chunk, expert) bases, expert offsets
+__global__ __launch_bounds__(1024) void k_scan(PermuteArgs a, int nchunks) {
+  __shared__ int sc[kMaxE];
+  __shared__ int sp[kMaxE];
+  const int E = a.E;
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      int *p = a.chunk_counts + (int64_t)c * E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+  }
+  sc[e] = (e < E) ? run : 0;
+  sp[e] = (e < E) ? ((run + 15) >> 4) << 4 : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scans over 1024 entries
+  for (int o = 1; o < kMaxE; o <<= 1) {
+    int x = (e >= o) ? sc[e - o] : 0;
+    int y = (e >= o) ? sp[e - o] : 0;
+    __syncthreads();
+    sc[e] += x;
+    sp[e] += y;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int excl = sc[e] - run;
+    a.expert_offsets[e] = excl;
+    if (a.padded_offsets) a.padded_offsets[e] = sp[e] - (((run + 15) >> 4) << 4);
+    if (e == E - 1) {
+      a.expert_offsets[E] = sc[e];
+      if (a.padded_offsets) a.padded_offsets[E] = sp[e];
+    }
+    for (int c = 0; c < nchunks; ++c) a.chunk_counts[(int64_t)c * E + e] += excl;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(PermuteArgs a) {
+  const int64_t R = a.T * a.k;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= R) return;
+  int e = a.topk_ids[f];
+  if (e < 0 || e >= a.E) e = 0;
+  const int64_t c = f / kPermuteChunk;
+  const int r = a.chunk_counts[c * a.E + e] + a.local_rank[f];
+  a.row_token[r] = (int)(f / a.k);
+  a.token_row[f] = r;
+}
+
+// one wave per permuted row: copy the packed codes and scale bytes of its token
+__global__ __launch_bounds__(256) void k_gather(PermuteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t R = a.T * a.k;
+  if (r >= R) return;
+  const int64_t t = a.row_token[r];
+  const int64_t cb = a.gather_K >> 1, sb = a.gather_K >> 4;
+  if ((cb & 15) == 0) {
+    const uint4 *s = reinterpret_cast<const uint4 *>(a.src_codes + t * cb);
+    uint4 *d = reinterpret_cast<uint4 *>(a.dst_codes + r * cb);
+    for (int64_t i = lane; i < (cb >> 4); i += kWave) d[i] = s[i];
+  } else {
+    for (int64_t i = lane; i < cb; i += kWave) a.dst_codes[r * cb + i] = a.src_codes[t * cb + i];
+  }
+  if ((sb & 3) == 0) {
+    const uint32_t *s = reinterpret_cast<const uint32_t *>(a.src_scales + t * sb);
+    uint32_t *d = reinterpret_cast<uint32_t *>(a.dst_scales + r * sb);
+    for (int64_t i = lane; i < (sb >> 2); i += kWave) d[i] = s[i];
+  } else {
+    for (int64_t i = lane; i < sb; i += kWave) a.dst_scales[r * sb + i] = a.src_scales[t * sb + i];
+  }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int64_t T, int E, int k) {
+  const int64_t R = T * k;
+  const int64_t nchunks = std::max<int64_t>(1, (R + kPermuteChunk - 1) / kPermuteChunk);
+  const size_t a = (size_t)nchunks * E * sizeof(int32_t);
+  const size_t b = (size_t)std::max<int64_t>(R, 1) * sizeof(int32_t);
+  return ((a + 255) & ~(size_t)255) + ((b + 255) & ~(size_t)255);
+}
+
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream) {
+  const int64_t R = a.T * a.k;
+  if (R == 0) {
+    // no assignment: all offsets are zero
+    PermuteArgs z = a;
+    k_scan<<<1, 1024, 0, stream>>>(z, 0);
+    return hipGetLastError();
+  }
+  const int nchunks = (int)((R + kPermuteChunk - 1) / kPermuteChunk);
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  if (a.logits) k_topk<<<(unsigned)((a.T + 3) / 4), 256, 0, stream>>>(a);
+  k_rank<<<nchunks, 64, 0, stream>>>(a, nbits);
+  k_scan<<<1, 1024, 0, stream>>>(a, nchunks);
+  k_scatter<<<(unsigned)((R + 255) / 256), 256, 0, stream>>>(a);
+  if (a.gather_K > 0) k_gather<<<(unsigned)((R + 3) / 4), 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace nv4

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/nv4moe.h declares, and its host-side validation rejects bad arguments
+with the documented status before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nv4moe.h")
+
+nv4 = pytest.importorskip("nvfp4_w4a4_moe_amd")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "for", "sizeof")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv4.LIB_PATH):
+        pytest.fail("libnv4moe.so is not built (run `python -c 'import __graft_entry__ as g; g.build()'`)")
+    return nv4.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"nvfp4_quantize", "moe_permute", "nvfp4_grouped_gemm", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == {"nv4_version", "nv4_status_string", "nv4_last_error", "nvfp4_quantize_workspace",
+                          "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
+                          "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine"}
+
+
+def test_binding_covers_every_symbol():
+    assert set(_declared_functions()) <= set(nv4._SIGS)
+
+
+def test_status_strings(lib):
+    assert lib.nv4_version() >= 100
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.nv4_status_string(s)
+
+
+def _q(lib, **kw):
+    d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, kw.get("orows", 32), kw.get("oK", 64), 0, 1)
+    return lib.nvfp4_quantize(ctypes.c_void_p(kw.get("x", 0x1000)), kw.get("xt", 0), kw.get("rows", 32),
+                              kw.get("K", 64), kw.get("ldx", 64), kw.get("layout", 1), kw.get("mode", 0),
+                              kw.get("nseg", 1), None, None, None, None, ctypes.byref(d),
+                              ctypes.c_void_p(0x1000), 1 << 20, None, None)
+
+
+def test_quantize_validation(lib):
+    assert _q(lib, K=40, ldx=40, oK=40) == -2          # K % 16
+    assert _q(lib, x=0x1008) == -2                      # x misaligned
+    assert _q(lib, ldx=68) == -2                        # row stride (136 bytes) not a 16-byte multiple
+    assert _q(lib, ldx=32) == -1                        # ldx < K
+    assert _q(lib, orows=31) == -1                      # out shape mismatch
+    assert _q(lib, layout=2, mode=2) == -3              # per-row scales only with rows layout
+    assert _q(lib, layout=7) == -1
+    assert _q(lib, xt=5) == -1
+    assert _q(lib, layout=3, nseg=3, orows=3 * 64, oK=32 // 3) == -2   # batched needs rows/nseg % 16 == 0
+    assert b"multiple of 16" in lib.nv4_last_error()
+    # NV4_COLS without segment offsets
+    assert _q(lib, layout=2, orows=64, oK=64) == -1
+    d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 32, 64, 0, 1)
+    assert lib.nvfp4_quantize(ctypes.c_void_p(0x1000), 0, 32, 64, 64, 1, 0, 1, None, None, None, None,
+                              ctypes.byref(d), None, 0, None, None) == -4      # no workspace
+
+
+def test_permute_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    args = lambda T, E, k, ws=P, wsb=1 << 20, ids=P: (None, T, E, k, 0, ids, P, P, P, P, P, None, None, ws, wsb,
+                                                      None, None)
+    assert lib.moe_permute(*args(16, 0, 1)) == -1
+    assert lib.moe_permute(*args(16, 2000, 2)) == -3
+    assert lib.moe_permute(*args(16, 8, 9)) == -3
+    assert lib.moe_permute(*args(16, 64, 33)) == -3
+    assert lib.moe_permute(*args(-1, 8, 2)) == -1
+    assert lib.moe_permute(*args(16, 8, 2, ids=None)) == -1
+    assert lib.moe_permute(*args(16, 8, 2, wsb=1)) == -4
+    assert lib.moe_permute_workspace(16384, 128, 8) >= 16384 * 8 * 4
+
+
+def test_gemm_validation(lib):
+    a = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 2048, 0, 1)
+    b = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 2048, 1, 8)
+    P = ctypes.c_void_p(0x1000)
+    g = lambda A, B, E=8, N=768, Mc=256, mode=0, epi=1, ldc=768: lib.nvfp4_grouped_gemm(
+        ctypes.byref(A), ctypes.byref(B), P, E, Mc, N, None, mode, epi, P, 1, ldc, None, None, 0, None)
+    assert g(a, b, N=700) == -1                 # B rows != E * 2N
+    assert g(a, b, ldc=100) == -1
+    assert g(a, b, Mc=257) == -1                # M_cap > rows of A
+    assert g(a, b, mode=1) == -3                # SwiGLU with GROUP_K
+    bk = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 2000, 1, 8)
+    assert g(a, bk) == -2                       # K mismatch
+    b7 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 2048, 1, 7)
+    assert g(a, b7) == -1                       # per-expert scales for 7 of 8 experts
+    a_seg = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 2048, 1, 8)
+    assert g(a_seg, b) == -3
+    assert g(a, b, E=0) == -1
+
+
+def test_combine_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.moe_combine(P, 1, 2048, P, P, 16, 8, 2046, P, 0, None) == -2
+    assert lib.moe_combine(P, 1, 2000, P, P, 16, 8, 2048, P, 0, None) == -2
+    assert lib.moe_combine(P, 3, 2048, P, P, 16, 8, 2048, P, 0, None) == -1
+    assert lib.moe_combine(ctypes.c_void_p(0x1004), 1, 2048, P, P, 16, 8, 2048, P, 0, None) == -2
