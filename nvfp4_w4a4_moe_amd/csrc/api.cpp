@@ -268,8 +268,9 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
     return fail(NV4_EINVAL, "nvfp4_grouped_gemm: NULL tensor buffer");
   if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4))
     return fail(NV4_EALIGN, "nvfp4_grouped_gemm: codes must be 16-byte and scales 4-byte aligned");
-  if (A->rows * (A->K / 2) >= (1ll << 40) || B->rows * (B->K / 2) >= (1ll << 40))
-    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: operand too large");
+  // the kernel addresses operands with 32-bit byte offsets and C with 32-bit element offsets
+  if (A->rows < 0 || B->rows < 0 || A->rows * (A->K / 2) >= (1ll << 32) || B->rows * (B->K / 2) >= (1ll << 32))
+    return fail(NV4_EINVAL, "nvfp4_grouped_gemm: each operand must stay below 4 GiB of codes");
   nv4::GemmArgs g{};
   g.a_codes = A->codes;
   g.a_scales = A->scales;
@@ -308,13 +309,15 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
     if (M_cap < 0 || (a_rows == nullptr && M_cap > A->rows))
       return fail(NV4_EINVAL, "nvfp4_grouped_gemm: M_cap exceeds the rows of A");
     if (ldc < N) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: ldc < N");
-    if (M_cap >= (1ll << 31)) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: M_cap must stay below 2^31");
+    if (M_cap * ldc >= (1ll << 31)) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: C must stay below 2^31 elements");
   } else {
     if (epilogue != NV4_EPI_NONE) return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K has no SwiGLU epilogue");
     if (a_rows) return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K takes no row index");
     if (A->scale_mode != NV4_SCALE_TENSOR || B->scale_mode != NV4_SCALE_TENSOR)
       return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: GROUP_K needs per-tensor scales");
     if (ldc < B->rows) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: ldc < rows of B");
+    if ((int64_t)E * A->rows * ldc >= (1ll << 31))
+      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: C must stay below 2^31 elements");
     g.N = B->rows;
   }
   return from_hip(nv4::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)), "nvfp4_grouped_gemm");

@@ -40,9 +40,11 @@ namespace {
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;
 
-template <int WAVES_M, int WAVES_N, int FM, int FN>
+template <int WAVES_M, int WAVES_N, int FM, int FN, int WAVES_PER_SIMD = 1, int STAGES = 2>
 struct TileCfg {
   static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N, kFM = FM, kFN = FN;
+  static constexpr int kWavesPerSimd = WAVES_PER_SIMD;  // occupancy the registers are budgeted for
+  static constexpr int kStages = STAGES;                // LDS ring depth (prefetch distance STAGES - 1)
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;  // rows of B per tile
   static constexpr int BK = 128;                // K per LDS stage
@@ -58,11 +60,47 @@ __device__ __forceinline__ int64_t min_row(int32_t idx, int64_t rows) {
   return idx < 0 ? 0 : (idx >= rows ? rows - 1 : idx);
 }
 
-// LDS position of 16-byte chunk q (0..3) of tile row r
-__device__ __forceinline__ int swz(int q, int r) { return q ^ ((r >> 1) & 3); }
+typedef __attribute__((address_space(3))) void *lds_ptr;
+// LDS DMA of N bytes per lane from the raw buffer [base, base + bytes) at byte
+// offset voff; lane i lands at dst + i * N.  Reads outside the buffer return zeros.
+// (Device-only helper: the buffer-resource type exists only on the GPU target.)
+__device__ __forceinline__ void dma16_to_lds(const void *base, uint32_t bytes, uint8_t *dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000), (lds_ptr)dst, 16,
+      voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void *base, uint32_t bytes, uint8_t *dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000), (lds_ptr)dst, 4,
+      voff, 0, 0, 0);
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left open)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence waits
+// for every outstanding memory operation, including LDS DMA of stages that are
+// still being prefetched.  Callers wait explicitly for what they need first.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS position of 16-byte chunk q (0..3) of tile row r (rows are 64 bytes).  A
+// fragment read has 16 consecutive rows read the same chunk in one LDS pass
+// (64 banks of 4 bytes); XOR-ing the chunk with bits 2..3 of the row gives those
+// 16 rows 16 distinct (row mod 4, position) bank groups.
+__device__ __forceinline__ int swz(int q, int r) { return q ^ ((r >> 2) & 3); }
 
 struct TileJob {
   int e;
+  bool gather;         // A rows come through the caller's row index
   int64_t m0, m_end;   // GROUP_M: rows of A/C; GROUP_K: rows of A (N dimension)
   int64_t n0;          // first B row of the tile (GROUP_K: first row of B)
   int64_t k_lo, k_hi;  // contraction range
@@ -102,12 +140,56 @@ __device__ void expert_tile_prefix(const int32_t *offsets, int E, int BM, int *t
   __syncthreads();
 }
 
+
+// Physical row of A for tile row r (-1 when outside the tile's range).
+__device__ __forceinline__ int64_t a_row_of(const GemmArgs &g, const TileJob &job, int r) {
+  const int64_t gr = job.m0 + r;
+  if (gr >= job.m_end) return -1;
+  if (job.gather) return min_row(g.a_rows_index[gr], g.a_rows);
+  return gr;
+}
+
+// Physical row of B for B-tile row r (-1 when outside N).  With the SwiGLU
+// epilogue a wave's FN fragments hold FN/2 gate fragments followed by the FN/2
+// up fragments of the same output columns.
+template <int GROUP, int EPI, int FN, int BN>
+__device__ __forceinline__ int64_t b_row_of(const GemmArgs &g, const TileJob &job, int64_t nt_idx, int r) {
+  if (GROUP == NV4_GROUP_K) {
+    const int64_t col = job.n0 + r;
+    return col < g.b_rows ? col : -1;
+  }
+  if (EPI == NV4_EPI_SWIGLU) {
+    constexpr int half = FN / 2;
+    const int wv = r / (FN * 32), f = (r % (FN * 32)) / 32;
+    const int64_t col = nt_idx * (BN / 2) + wv * (half * 32) + (f % half) * 32 + (r & 31);
+    if (col >= g.N) return -1;
+    return (int64_t)job.e * 2 * g.N + (f >= half ? g.N : 0) + col;
+  }
+  const int64_t col = nt_idx * BN + r;
+  return col < g.N ? (int64_t)job.e * g.N + col : -1;
+}
+
 template <class Cfg, int GROUP, int EPI, bool OUT_F32, bool A_ROW_SCALE>
-__global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads;
+__global__ __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerSimd)))
+void k_gemm(GemmArgs g) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads, NW = NT / 64;
   constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
   constexpr int RB = Cfg::kRowBytes, SB = Cfg::kScBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Cfg::kStageBytes];
+  // LDS DMA plan: codes in 1 KB blocks of 16 rows, scales in 256-byte blocks of 32
+  // rows (A rows first, then B rows); wave w issues blocks w, w + NW, ...
+  constexpr int kCodeBlocks = (BM + BN) / 16, kScBlocks = (BM + BN) / 32;
+  constexpr int kCodeIters = (kCodeBlocks + NW - 1) / NW;
+  constexpr int kScIters = (kScBlocks + NW - 1) / NW;
+  // DMAs every wave issues per stage (the vmcnt wait uses the smallest count)
+  constexpr int kDmaMin = kCodeBlocks / NW + kScBlocks / NW;
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows must be multiples of 32");
+  constexpr int kScBase = (BM + BN) * RB;
+  constexpr int S = Cfg::kStages;
+  static_assert(S >= 2 && S <= 4, "LDS ring of 2 to 4 stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[Cfg::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[Cfg::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? Cfg::kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? Cfg::kStageBytes : 16];
   __shared__ int tstart[kMaxExperts + 1];
   __shared__ int scratch[NT];
 
@@ -117,6 +199,9 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
   const int E = g.E;
   const int64_t K = g.K;
   const int64_t ldA = K >> 1, ldAs = K >> 4;  // bytes per row: codes, scales
+  // buffer resources: loads past num_records return zeros (operands are < 4 GiB)
+  const uint32_t na_c = (uint32_t)(g.a_rows * ldA), na_s = (uint32_t)(g.a_rows * ldAs);
+  const uint32_t nb_c = (uint32_t)(g.b_rows * ldA), nb_s = (uint32_t)(g.b_rows * ldAs);
 
   // ---- tile space
   int64_t total;
@@ -147,7 +232,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
     if (GROUP == NV4_GROUP_M) {
       const int64_t mt = L / ntn;
       nt_idx = L - mt * ntn;
-      int lo = 0, hi = E - 1;  // last expert with tstart[e] <= mt
+      int lo = 0, hi = E - 1;  // last expert with tstart[e] <= mt (it owns >= 1 tile)
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (tstart[mid] <= mt) lo = mid; else hi = mid - 1;
@@ -155,10 +240,12 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
       job.e = lo;
       job.m0 = g.offsets[lo] + (mt - tstart[lo]) * BM;
       job.m_end = std::min<int64_t>(g.offsets[lo + 1], g.M_cap);  // never past the caller's C rows
-      job.n0 = nt_idx;  // resolved per row below
+      job.n0 = nt_idx;
       job.k_lo = 0;
       job.k_hi = K;
+      job.gather = g.a_rows_index != nullptr;
     } else {
+      job.gather = false;
       const int tn = (int)((g.a_rows + BM - 1) / BM);
       const int64_t per_e = (int64_t)tn * ntn;
       job.e = (int)(L / per_e);
@@ -172,141 +259,57 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
       job.k_hi = g.offsets[job.e + 1];
     }
 
-    // ---- per-thread load assignments (fixed for the tile)
-    // codes: (BM + BN) rows x 4 chunks of 16 bytes
-    constexpr int kChunks = (BM + BN) * 4;
-    constexpr int kChunkIters = (kChunks + NT - 1) / NT;
-    const uint8_t *src_c[kChunkIters];
-    int lds_c[kChunkIters];
-    bool ok_c[kChunkIters];
+    // ---- this lane's DMA sources: byte offsets into the operand; rows outside the
+    // tile's range point past the end of the operand, so they load as zeros.
+    uint32_t c_off[kCodeIters];
 #pragma unroll
-    for (int i = 0; i < kChunkIters; ++i) {
-      const int id = tid + i * NT;
-      const int row = id >> 2, q = id & 3;
-      src_c[i] = nullptr;
-      lds_c[i] = 0;
-      ok_c[i] = false;
-      if (id < kChunks) {
-        if (row < BM) {
-          const int64_t gr = job.m0 + row;
-          if (gr < job.m_end) {
-            int64_t pr = gr;
-            if (GROUP == NV4_GROUP_M && g.a_rows_index) pr = min_row(g.a_rows_index[gr], g.a_rows);
-            src_c[i] = g.a_codes + pr * ldA + q * 16;
-            ok_c[i] = true;
-          }
-          lds_c[i] = row * RB + swz(q, row) * 16;
-        } else {
-          const int br = row - BM;
-          int64_t grow = -1;
-          if (GROUP == NV4_GROUP_M) {
-            if (EPI == NV4_EPI_SWIGLU) {
-              const int wv = br / (FN * 32), f = (br % (FN * 32)) / 32;
-              const int half = FN / 2;
-              const int64_t col = nt_idx * (BN / 2) + wv * (half * 32) + (f % half) * 32 + (br & 31);
-              if (col < g.N) grow = (int64_t)job.e * 2 * g.N + (f >= half ? g.N : 0) + col;
-            } else {
-              const int64_t col = nt_idx * BN + br;
-              if (col < g.N) grow = (int64_t)job.e * g.N + col;
-            }
-          } else {
-            const int64_t col = job.n0 + br;
-            if (col < g.b_rows) grow = col;
-          }
-          if (grow >= 0) {
-            src_c[i] = g.b_codes + grow * ldA + q * 16;
-            ok_c[i] = true;
-          }
-          lds_c[i] = BM * RB + br * RB + swz(q, br) * 16;
-        }
-      }
+    for (int j = 0; j < kCodeIters; ++j) {
+      const int row = (j * NW + wave) * 16 + (lane >> 2);
+      const bool isA = row < BM;  // uniform over the wave
+      const int r = isA ? row : row - BM;
+      const int q = swz(lane & 3, r);  // chunk that lands in this lane's slot (swz is its own inverse)
+      int64_t pr = -1;
+      if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
+      c_off[j] = pr >= 0 ? (uint32_t)(pr * ldA) + q * 16 : (isA ? na_c : nb_c);
     }
-    // scale bytes: (BM + BN) rows x 8 bytes (two dwords)
-    constexpr int kScIters = ((BM + BN) + NT - 1) / NT;
-    const uint8_t *src_s[kScIters];
-    int lds_s[kScIters];
+    uint32_t s_off[kScIters];
 #pragma unroll
-    for (int i = 0; i < kScIters; ++i) {
-      const int row = tid + i * NT;
-      src_s[i] = nullptr;
-      lds_s[i] = -1;
-      if (row < BM + BN) {
-        if (row < BM) {
-          const int64_t gr = job.m0 + row;
-          if (gr < job.m_end) {
-            int64_t pr = gr;
-            if (GROUP == NV4_GROUP_M && g.a_rows_index) pr = min_row(g.a_rows_index[gr], g.a_rows);
-            src_s[i] = g.a_scales + pr * ldAs;
-          }
-        } else {
-          const int br = row - BM;
-          int64_t grow = -1;
-          if (GROUP == NV4_GROUP_M) {
-            if (EPI == NV4_EPI_SWIGLU) {
-              const int wv = br / (FN * 32), f = (br % (FN * 32)) / 32;
-              const int half = FN / 2;
-              const int64_t col = nt_idx * (BN / 2) + wv * (half * 32) + (f % half) * 32 + (br & 31);
-              if (col < g.N) grow = (int64_t)job.e * 2 * g.N + (f >= half ? g.N : 0) + col;
-            } else {
-              const int64_t col = nt_idx * BN + br;
-              if (col < g.N) grow = (int64_t)job.e * g.N + col;
-            }
-          } else {
-            const int64_t col = job.n0 + br;
-            if (col < g.b_rows) grow = col;
-          }
-          if (grow >= 0) src_s[i] = g.b_scales + grow * ldAs;
-        }
-        lds_s[i] = (BM + BN) * RB + row * SB;
-      }
+    for (int j = 0; j < kScIters; ++j) {
+      const int row = (j * NW + wave) * 32 + (lane >> 1);
+      const bool isA = row < BM;
+      const int r = isA ? row : row - BM;
+      int64_t pr = -1;
+      if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
+      s_off[j] = pr >= 0 ? (uint32_t)(pr * ldAs) + (lane & 1) * 4 : (isA ? na_s : nb_s);
     }
 
-    // ---- K range in stages of BK (stage starts 128-aligned; blocks outside [k_lo, k_hi) are masked)
+    // ---- K range in stages of BK (stage starts 128-aligned; blocks outside
+    // [k_lo, k_hi) get scale 0 when read, so they contribute nothing)
     const int64_t kb0 = (job.k_lo / BK) * BK;
     const int nk = job.k_hi > job.k_lo ? (int)((job.k_hi - kb0 + BK - 1) / BK) : 0;
 
-    uint4 rc[kChunkIters];
-    uint2 rs[kScIters];
-    auto gload = [&](int kt) {
-      const int64_t k0 = kb0 + (int64_t)kt * BK;
+    auto issue = [&](int kt, uint8_t *dst) {
+      const uint32_t kc = (uint32_t)((kb0 + (int64_t)kt * BK) >> 1);  // code byte offset of the stage
+      const uint32_t ks = (uint32_t)((kb0 + (int64_t)kt * BK) >> 4);  // scale byte offset of the stage
 #pragma unroll
-      for (int i = 0; i < kChunkIters; ++i) {
-        const int q = (tid + i * NT) & 3;
-        const int64_t kk = k0 + q * 32;
-        if (ok_c[i] && kk < K) rc[i] = *reinterpret_cast<const uint4 *>(src_c[i] + (k0 >> 1));
-        else rc[i] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < kCodeIters; ++j) {
+        const int blk = j * NW + wave;
+        if (kCodeBlocks % NW != 0 && blk >= kCodeBlocks) break;
+        const bool isA = blk * 16 < BM;
+        // a chunk past the row end reads the next row (finite codes); the scale
+        // mask in compute() zeroes those blocks.  Past the operand's end the buffer
+        // returns zeros.
+        if (isA) dma16_to_lds(g.a_codes, na_c, dst + blk * 1024, c_off[j] + kc);
+        else dma16_to_lds(g.b_codes, nb_c, dst + blk * 1024, c_off[j] + kc);
       }
 #pragma unroll
-      for (int i = 0; i < kScIters; ++i) {
-        uint2 v = make_uint2(0, 0);
-        if (src_s[i]) {
-          const uint32_t *p = reinterpret_cast<const uint32_t *>(src_s[i] + (k0 >> 4));
-          if (k0 < K) v.x = p[0];
-          if (k0 + 64 < K) v.y = p[1];
-          // mask blocks outside [k_lo, k_hi): their scale becomes 0, so they decode to 0
-          if (GROUP == NV4_GROUP_K) {
-            uint32_t mlo = 0, mhi = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int64_t kbl = k0 + b * 16, kbh = k0 + 64 + b * 16;
-              if (kbl >= job.k_lo && kbl < job.k_hi) mlo |= 0xFFu << (8 * b);
-              if (kbh >= job.k_lo && kbh < job.k_hi) mhi |= 0xFFu << (8 * b);
-            }
-            v.x &= mlo;
-            v.y &= mhi;
-          }
-        }
-        rs[i] = v;
+      for (int j = 0; j < kScIters; ++j) {
+        const int blk = j * NW + wave;
+        if (kScBlocks % NW != 0 && blk >= kScBlocks) break;
+        const bool isA = blk * 32 < BM;
+        if (isA) dma4_to_lds(g.a_scales, na_s, dst + kScBase + blk * 256, s_off[j] + ks);
+        else dma4_to_lds(g.b_scales, nb_s, dst + kScBase + blk * 256, s_off[j] + ks);
       }
-    };
-    auto sstore = [&](int buf) {
-      uint8_t *base = lds + buf * Cfg::kStageBytes;
-#pragma unroll
-      for (int i = 0; i < kChunkIters; ++i)
-        if (tid + i * NT < kChunks) *reinterpret_cast<uint4 *>(base + lds_c[i]) = rc[i];
-#pragma unroll
-      for (int i = 0; i < kScIters; ++i)
-        if (lds_s[i] >= 0) *reinterpret_cast<uint2 *>(base + lds_s[i]) = rs[i];
     };
 
     f32x16 acc[FM][FN];
@@ -317,91 +320,150 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (nk > 0) {
-      gload(0);
-      sstore(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) gload(kt + 1);
-      const uint8_t *base = lds + (kt & 1) * Cfg::kStageBytes;
-      const uint8_t *sbase = base + (BM + BN) * RB;
-#pragma unroll
-      for (int sub = 0; sub < BK / 64; ++sub) {
-        uint4 ca[FM], cb[FN];
-        f16x2 sa[FM], sbv[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = wm * FM * 32 + i * 32 + l32;
-          ca[i] = *reinterpret_cast<const uint4 *>(base + row * RB + swz(sub * 2 + h, row) * 16);
-          const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + row * SB + sub * 4 + 2 * h);
-          sa[i] = e4m3x2_to_f16(s2);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * FN * 32 + j * 32 + l32;
-          cb[j] = *reinterpret_cast<const uint4 *>(base + BM * RB + row * RB + swz(sub * 2 + h, row) * 16);
-          const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + (BM + row) * SB + sub * 4 + 2 * h);
-          sbv[j] = e4m3x2_to_f16(s2);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          f16x8 av[FM], bv[FN];
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const uint32_t w = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
-            const _Float16 sc = (s < 2) ? sa[i][0] : sa[i][1];
-            av[i] = decode8_f16(w, f16x2{sc, sc});
-          }
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const uint32_t w = s == 0 ? cb[j].x : s == 1 ? cb[j].y : s == 2 ? cb[j].z : cb[j].w;
-            const _Float16 sc = (s < 2) ? sbv[j][0] : sbv[j][1];
-            bv[j] = decode8_f16(w, f16x2{sc, sc});
-          }
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        }
+    // LDS stage layout: per 64-wide K slice ("sub"), every fragment row reads 32
+    // codes (one 16-byte LDS read) and two scale bytes; MFMA step t = sub*4 + s
+    // consumes dword s of those codes with the scale of block s/2.
+    constexpr int kSubs = BK / 64, kSteps = BK / 16;
+    uint4 ca[kSubs][FM], cb[kSubs][FN];
+    f16x2 sa[kSubs][FM], sbv[kSubs][FN];
+    auto lds_read = [&](int sub, const uint8_t *base, int kt) {
+      const int64_t k0 = kb0 + (int64_t)kt * BK;
+      const bool full = k0 >= job.k_lo && k0 + BK <= job.k_hi;
+      const uint8_t *sbase = base + kScBase;
+      // scale-byte mask of this lane's two blocks (k0 + sub*64 + h*32 + {0, 16}):
+      // blocks outside [k_lo, k_hi) decode to zero
+      uint32_t smask = 0xFFFFu;
+      if (!full) {
+        const int64_t kb = k0 + sub * 64 + h * 32;
+        smask = ((kb >= job.k_lo && kb < job.k_hi) ? 0x00FFu : 0u) |
+                ((kb + 16 >= job.k_lo && kb + 16 < job.k_hi) ? 0xFF00u : 0u);
       }
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
-      __syncthreads();
-    }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * FM * 32 + i * 32 + l32;
+        ca[sub][i] = *reinterpret_cast<const uint4 *>(base + row * RB + swz(sub * 2 + h, row) * 16);
+        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + row * SB + sub * 4 + 2 * h);
+        sa[sub][i] = e4m3x2_to_f16(s2 & smask);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * FN * 32 + j * 32 + l32;
+        cb[sub][j] = *reinterpret_cast<const uint4 *>(base + BM * RB + row * RB + swz(sub * 2 + h, row) * 16);
+        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + (BM + row) * SB + sub * 4 + 2 * h);
+        sbv[sub][j] = e4m3x2_to_f16(s2 & smask);
+      }
+    };
+    auto decode = [&](int t, f16x8 (&av)[FM], f16x8 (&bv)[FN]) {
+      const int sub = t >> 2, st = t & 3;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t w = st == 0 ? ca[sub][i].x : st == 1 ? ca[sub][i].y : st == 2 ? ca[sub][i].z : ca[sub][i].w;
+        const f16x2 sc = st < 2 ? __builtin_shufflevector(sa[sub][i], sa[sub][i], 0, 0)
+                                : __builtin_shufflevector(sa[sub][i], sa[sub][i], 1, 1);
+        av[i] = decode8_f16(w, sc);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t w = st == 0 ? cb[sub][j].x : st == 1 ? cb[sub][j].y : st == 2 ? cb[sub][j].z : cb[sub][j].w;
+        const f16x2 sc = st < 2 ? __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 0, 0)
+                                : __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 1, 1);
+        bv[j] = decode8_f16(w, sc);
+      }
+    };
+    auto mfmas = [&](const f16x8 (&av)[FM], const f16x8 (&bv)[FN]) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    };
+    // wait until this wave's LDS DMA of stage `need` is done, given that `after`
+    // more stages were issued after it
+    auto wait_stage = [&](int after) {
+      if (after >= 2) wait_vmcnt<2 * kDmaMin>();
+      else if (after == 1) wait_vmcnt<kDmaMin>();
+      else wait_vmcnt<0>();
+    };
+    auto bufp = [&](int b) -> uint8_t * { return b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : lds3; };
 
-    // ---- epilogue
+    // K loop over an LDS ring of S stages (stage kt+S-1 streams in by LDS DMA while
+    // stage kt is computed); unrolled by S so that every buffer is a fixed LDS object.
+    for (int s0 = 0; s0 < S - 1; ++s0)
+      if (s0 < nk) issue(s0, bufp(s0));
+    {
+      auto stage = [&](const int B, int kt) {  // B = kt % S, a literal at every call
+        wait_stage(std::min(S - 2, nk - 1 - kt));
+        block_barrier();
+        if (kt + S - 1 < nk) issue(kt + S - 1, bufp((B + S - 1) % S));
+        const uint8_t *base = bufp(B);
+#pragma unroll
+        for (int sub = 0; sub < kSubs; ++sub) lds_read(sub, base, kt);
+#pragma unroll
+        for (int t = 0; t < kSteps; ++t) {
+          f16x8 av[FM], bv[FN];
+          decode(t, av, bv);
+          mfmas(av, bv);
+        }
+      };
+      for (int kt = 0; kt < nk; kt += S) {
+        stage(0, kt);
+        if (kt + 1 < nk) stage(1, kt + 1);
+        if (S > 2 && kt + 2 < nk) stage(2 % S, kt + 2);
+        if (S > 3 && kt + 3 < nk) stage(3 % S, kt + 3);
+      }
+    }
+    // every LDS read of this tile has been consumed; the next tile refills the ring
+    block_barrier();
+
+    // ---- epilogue: tensor scales, optional SwiGLU, store (32-bit element offsets;
+    // the caller's C is below 2^31 elements)
     float b_ts = 1.0f;
     if (GROUP == NV4_GROUP_M) b_ts = g.b_scale_mode == NV4_SCALE_SEGMENT ? g.b_tscale[job.e] : g.b_tscale[0];
     else b_ts = g.b_tscale[0];
+    const int ldc = (int)g.ldc;
+    const int row0 = (int)job.m0 + wm * FM * 32 + h * 4;
+    const int rows_left = (int)(job.m_end - job.m0) - wm * FM * 32 - h * 4;  // rows r with r < rows_left are valid
+    int col0, ncols;
+    if (EPI == NV4_EPI_SWIGLU) {
+      col0 = (int)nt_idx * (BN / 2) + wn * (FN / 2 * 32) + l32;
+      ncols = (int)g.N;
+    } else if (GROUP == NV4_GROUP_M) {
+      col0 = (int)nt_idx * BN + wn * FN * 32 + l32;
+      ncols = (int)g.N;
+    } else {
+      col0 = (int)job.n0 + wn * FN * 32 + l32;
+      ncols = (int)g.b_rows;
+    }
+    const int cbase = GROUP == NV4_GROUP_K ? job.e * (int)g.a_rows * ldc : 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rloc = wm * FM * 32 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        const int64_t grow = job.m0 + rloc;
-        if (grow >= job.m_end) continue;
+        const int rl = i * 32 + (r >> 2) * 8 + (r & 3);
+        if (rl >= rows_left) continue;
+        const int grow = row0 + rl;
         float sc = a_ts * b_ts;
         if (A_ROW_SCALE) {
-          int64_t pr = grow;
-          if (g.a_rows_index) pr = min_row(g.a_rows_index[grow], g.a_rows);
+          const int64_t pr = job.gather ? min_row(g.a_rows_index[grow], g.a_rows) : grow;
           sc = g.a_tscale[pr] * b_ts;
         }
+        const int rbase = cbase + grow * ldc;
         if (EPI == NV4_EPI_SWIGLU) {
 #pragma unroll
           for (int j = 0; j < FN / 2; ++j) {
-            const int64_t col = nt_idx * (BN / 2) + wn * (FN / 2 * 32) + j * 32 + l32;
-            if (col >= g.N) continue;
+            const int col = col0 + j * 32;
+            if (col >= ncols) continue;
             const float gt = acc[i][j][r] * sc;
             const float up = acc[i][j + FN / 2][r] * sc;
-            const float hv = gt / (1.0f + expf(-gt)) * up;
+            // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
+            const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             float stored;
             if (OUT_F32) {
-              reinterpret_cast<float *>(g.C)[grow * g.ldc + col] = hv;
+              reinterpret_cast<float *>(g.C)[rbase + col] = hv;
               stored = hv;
             } else {
               const uint32_t b16 = f32_to_bf16_rne(hv);
-              reinterpret_cast<uint16_t *>(g.C)[grow * g.ldc + col] = (uint16_t)b16;
+              reinterpret_cast<uint16_t *>(g.C)[rbase + col] = (uint16_t)b16;
               stored = bf16_bits_to_f32(b16);
             }
             amax_run = fmaxf(amax_run, fabsf(stored));
@@ -409,19 +471,11 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            int64_t col, off;
-            if (GROUP == NV4_GROUP_M) {
-              col = nt_idx * BN + wn * FN * 32 + j * 32 + l32;
-              if (col >= g.N) continue;
-              off = grow * g.ldc + col;
-            } else {
-              col = job.n0 + wn * FN * 32 + j * 32 + l32;
-              if (col >= g.b_rows) continue;
-              off = ((int64_t)job.e * g.a_rows + grow) * g.ldc + col;
-            }
+            const int col = col0 + j * 32;
+            if (col >= ncols) continue;
             const float v = acc[i][j][r] * sc;
-            if (OUT_F32) reinterpret_cast<float *>(g.C)[off] = v;
-            else reinterpret_cast<uint16_t *>(g.C)[off] = (uint16_t)f32_to_bf16_rne(v);
+            if (OUT_F32) reinterpret_cast<float *>(g.C)[rbase + col] = v;
+            else reinterpret_cast<uint16_t *>(g.C)[rbase + col] = (uint16_t)f32_to_bf16_rne(v);
           }
         }
       }
@@ -433,15 +487,20 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_gemm(GemmArgs g) {
   }
 }
 
-using Cfg128 = TileCfg<2, 2, 2, 2>;
+// Tile: 128 rows of A x 256 rows of B per workgroup, 4 waves of 128 x 64, two
+// workgroups per CU (two waves per SIMD, from different workgroups, so that one
+// wave's FP16 decode overlaps the other's MFMAs), double-buffered LDS stages.
+// 128-row tiles keep the padding of ragged expert segments small.
+using GemmTile = TileCfg<1, 4, 4, 2, 2, 2>;
 
 template <int GROUP, int EPI, bool OUT_F32, bool ROWS>
-hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream) {
+hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
+  using Cfg = GemmTile;
   const int cus = device_cu_count();
-  int grid = cus * 4;
+  int grid = cus * 2;  // two resident workgroups per CU (LDS and registers allow two)
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
-  k_gemm<Cfg128, GROUP, EPI, OUT_F32, ROWS><<<grid, Cfg128::kThreads, 0, stream>>>(g);
+  k_gemm<Cfg, GROUP, EPI, OUT_F32, ROWS><<<grid, Cfg::kThreads, 0, stream>>>(g);
   return hipGetLastError();
 }
 
@@ -450,19 +509,19 @@ hipError_t launch_cfg(const GemmArgs &g, hipStream_t stream) {
 hipError_t launch_grouped_gemm(const GemmArgs &g, hipStream_t stream) {
   const bool rows = g.a_scale_mode == NV4_SCALE_ROW;
   if (g.group_mode == NV4_GROUP_K) {
-    return g.c_is_f32 ? launch_cfg<NV4_GROUP_K, NV4_EPI_NONE, true, false>(g, stream)
-                      : launch_cfg<NV4_GROUP_K, NV4_EPI_NONE, false, false>(g, stream);
+    return g.c_is_f32 ? launch_tile<NV4_GROUP_K, NV4_EPI_NONE, true, false>(g, stream)
+                      : launch_tile<NV4_GROUP_K, NV4_EPI_NONE, false, false>(g, stream);
   }
   if (g.epilogue == NV4_EPI_SWIGLU) {
-    if (rows) return g.c_is_f32 ? launch_cfg<NV4_GROUP_M, NV4_EPI_SWIGLU, true, true>(g, stream)
-                                : launch_cfg<NV4_GROUP_M, NV4_EPI_SWIGLU, false, true>(g, stream);
-    return g.c_is_f32 ? launch_cfg<NV4_GROUP_M, NV4_EPI_SWIGLU, true, false>(g, stream)
-                      : launch_cfg<NV4_GROUP_M, NV4_EPI_SWIGLU, false, false>(g, stream);
+    if (rows) return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, true, true>(g, stream)
+                                : launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, false, true>(g, stream);
+    return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, true, false>(g, stream)
+                      : launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, false, false>(g, stream);
   }
-  if (rows) return g.c_is_f32 ? launch_cfg<NV4_GROUP_M, NV4_EPI_NONE, true, true>(g, stream)
-                              : launch_cfg<NV4_GROUP_M, NV4_EPI_NONE, false, true>(g, stream);
-  return g.c_is_f32 ? launch_cfg<NV4_GROUP_M, NV4_EPI_NONE, true, false>(g, stream)
-                    : launch_cfg<NV4_GROUP_M, NV4_EPI_NONE, false, false>(g, stream);
+  if (rows) return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_NONE, true, true>(g, stream)
+                              : launch_tile<NV4_GROUP_M, NV4_EPI_NONE, false, true>(g, stream);
+  return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_NONE, true, false>(g, stream)
+                    : launch_tile<NV4_GROUP_M, NV4_EPI_NONE, false, false>(g, stream);
 }
 
 }  // namespace nv4
