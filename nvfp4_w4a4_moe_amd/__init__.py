@@ -180,7 +180,8 @@ def moe_permute(logits: torch.Tensor | None, E: int, k: int, T: int | None = Non
                 topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
                 gather_src: NVFP4 | None = None, gather_dst: NVFP4 | None = None,
                 ws: torch.Tensor | None = None, dev_status: torch.Tensor | None = None,
-                stream=None, device="cuda") -> Routing:
+                stream=None, device="cuda", out: Routing | None = None) -> Routing:
+    """Route (when logits are given) and permute.  With `out`, its buffers are reused."""
     lib = load()
     if logits is not None:
         assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.shape[1] == E
@@ -189,14 +190,21 @@ def moe_permute(logits: torch.Tensor | None, E: int, k: int, T: int | None = Non
     elif topk_ids is not None:
         T = topk_ids.shape[0]
         device = topk_ids.device
+    if out is not None:
+        if topk_ids is None:
+            topk_ids = out.topk_ids
+        if topk_w is None and logits is not None:
+            topk_w = out.topk_w
+        offsets, padded, row_token, token_row = out.offsets, out.padded_offsets, out.row_token, out.token_row
+    else:
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+        padded = torch.empty((E + 1,), dtype=torch.int32, device=device)
+        row_token = torch.empty((T * k,), dtype=torch.int32, device=device)
+        token_row = torch.empty((T, k), dtype=torch.int32, device=device)
     if topk_ids is None:
         topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
     if topk_w is None and logits is not None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
-    offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
-    padded = torch.empty((E + 1,), dtype=torch.int32, device=device)
-    row_token = torch.empty((T * k,), dtype=torch.int32, device=device)
-    token_row = torch.empty((T, k), dtype=torch.int32, device=device)
     if ws is None:
         ws = torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device)
     gs = ctypes.byref(gather_src.c()) if gather_src is not None else None
@@ -331,11 +339,11 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
         nvfp4_quantize(x, out=bufs.xq, ws=bufs.qws, stream=stream)
     with _Stage(stage_events, "route_permute", st):
         if fuse_gather:
-            bufs.routing = moe_permute(logits, w.E, k, ws=bufs.pws, stream=stream)
+            bufs.routing = moe_permute(logits, w.E, k, ws=bufs.pws, stream=stream, out=bufs.routing)
             a, a_rows = bufs.xq, bufs.routing.row_token
         else:
             bufs.routing = moe_permute(logits, w.E, k, gather_src=bufs.xq, gather_dst=bufs.xg, ws=bufs.pws,
-                                       stream=stream)
+                                       stream=stream, out=bufs.routing)
             bufs.xg.tscale = bufs.xq.tscale
             a, a_rows = bufs.xg, None
     with _Stage(stage_events, "gemm1_swiglu", st):

@@ -16,14 +16,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool Y_F32, bool OUT_F32>
+// KC > 0: k is the compile-time constant KC (all k row loads in flight together)
+template <bool Y_F32, bool OUT_F32, int KC>
 __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
   const int64_t t = blockIdx.x;
-  const int32_t *tr = a.token_row + t * a.k;
-  const float *tw = a.topk_w + t * a.k;
+  const int k = KC > 0 ? KC : a.k;
+  const int32_t *tr = a.token_row + t * k;
+  const float *tw = a.topk_w + t * k;
   for (int64_t c = (int64_t)threadIdx.x * 4; c < a.H; c += kThreads * 4) {
     float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
+#pragma unroll
+    for (int j = 0; j < k; ++j) {
       const int64_t r = tr[j];
       const float w = tw[j];
       float y0, y1, y2, y3;
@@ -52,15 +55,26 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
-  if (a.T == 0) return hipSuccess;
+template <int KC>
+void launch_k(const CombineArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.T;
   if (a.y_is_f32) {
-    if (a.out_is_f32) k_combine<true, true><<<grid, kThreads, 0, stream>>>(a);
-    else k_combine<true, false><<<grid, kThreads, 0, stream>>>(a);
+    if (a.out_is_f32) k_combine<true, true, KC><<<grid, kThreads, 0, stream>>>(a);
+    else k_combine<true, false, KC><<<grid, kThreads, 0, stream>>>(a);
   } else {
-    if (a.out_is_f32) k_combine<false, true><<<grid, kThreads, 0, stream>>>(a);
-    else k_combine<false, false><<<grid, kThreads, 0, stream>>>(a);
+    if (a.out_is_f32) k_combine<false, true, KC><<<grid, kThreads, 0, stream>>>(a);
+    else k_combine<false, false, KC><<<grid, kThreads, 0, stream>>>(a);
+  }
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
+  if (a.T == 0) return hipSuccess;
+  switch (a.k) {
+    case 1: launch_k<1>(a, stream); break;
+    case 2: launch_k<2>(a, stream); break;
+    case 4: launch_k<4>(a, stream); break;
+    case 8: launch_k<8>(a, stream); break;
+    default: launch_k<0>(a, stream); break;
   }
   return hipGetLastError();
 }

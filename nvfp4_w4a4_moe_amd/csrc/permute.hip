@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
       const int oi = __shfl_xor(bi, o, kWave);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);  // (bi == INT_MAX only if every remaining logit is NaN)
     const float w = expf(bv - mx) / s;
     wsum += w;
     if (lane == j) { my_id = bi; my_w = w; }
@@ -125,43 +125,67 @@ __global__ __launch_bounds__(64) void k_rank(PermuteArgs a, int nbits) {
   if (badid && a.dev_status) atomicOr(a.dev_status, kDsBadExpert);
 }
 
-// one workgroup: chunk histograms -> per-(chunk, expert) bases, expert offsets
+// one workgroup: chunk histograms -> per-(chunk, expert) bases, expert offsets.
+// Each wave takes experts w, w + 16, ...: its lanes hold consecutive chunk counts
+// of the expert and a wave-wide exclusive scan gives the chunk bases; then one
+// block-wide scan over the expert totals gives the offsets.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o, kWave);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void k_scan(PermuteArgs a, int nchunks) {
   __shared__ int sc[kMaxE];
   __shared__ int sp[kMaxE];
+  __shared__ int tot[kMaxE];
   const int E = a.E;
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // 1. per expert: exclusive prefix over chunks (in place), total
+  for (int e = wave; e < E; e += 16) {
+    int run = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const int c = c0 + lane;
       int *p = a.chunk_counts + (int64_t)c * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+      const int v = c < nchunks ? *p : 0;
+      const int incl = wave_incl_scan(v, lane);
+      if (c < nchunks) *p = run + incl - v;
+      run += __shfl(incl, 63, kWave);
     }
+    if (lane == 0) tot[e] = run;
   }
-  sc[e] = (e < E) ? run : 0;
-  sp[e] = (e < E) ? ((run + 15) >> 4) << 4 : 0;
   __syncthreads();
-  // inclusive Hillis-Steele scans over 1024 entries
+  // 2. exclusive scans over experts (counts and 16-padded counts)
+  const int e = tid;
+  const int run = e < E ? tot[e] : 0;
+  const int prun = ((run + 15) >> 4) << 4;
+  sc[e] = run;
+  sp[e] = prun;
+  __syncthreads();
   for (int o = 1; o < kMaxE; o <<= 1) {
-    int x = (e >= o) ? sc[e - o] : 0;
-    int y = (e >= o) ? sp[e - o] : 0;
+    const int x = (e >= o) ? sc[e - o] : 0;
+    const int y = (e >= o) ? sp[e - o] : 0;
     __syncthreads();
     sc[e] += x;
     sp[e] += y;
     __syncthreads();
   }
   if (e < E) {
-    const int excl = sc[e] - run;
-    a.expert_offsets[e] = excl;
-    if (a.padded_offsets) a.padded_offsets[e] = sp[e] - (((run + 15) >> 4) << 4);
+    a.expert_offsets[e] = sc[e] - run;
+    if (a.padded_offsets) a.padded_offsets[e] = sp[e] - prun;
     if (e == E - 1) {
       a.expert_offsets[E] = sc[e];
       if (a.padded_offsets) a.padded_offsets[E] = sp[e];
     }
-    for (int c = 0; c < nchunks; ++c) a.chunk_counts[(int64_t)c * E + e] += excl;
+    tot[e] = sc[e] - run;  // exclusive offset of expert e
   }
+  __syncthreads();
+  // 3. chunk bases become absolute rows
+  const int64_t n = (int64_t)nchunks * E;
+  for (int64_t i = tid; i < n; i += 1024) a.chunk_counts[i] += tot[i % E];
 }
 
 __global__ __launch_bounds__(256) void k_scatter(PermuteArgs a) {

@@ -66,40 +66,40 @@ __global__ void k_fill_zero(float *p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Group amax: one wave per row (rows strided over the grid); the running max of
-// the wave's current group is flushed with an order-independent atomic max.
-__global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  int cur = -1;
+// Group amax.  Workgroup (p, g) scans rows p, p + P, ... of group g's row range
+// (an equal split of the rows, or [seg_offsets[g], seg_offsets[g+1])); its
+// waves reduce in registers and LDS, and one order-independent atomic max per
+// workgroup goes to amax_acc[g], so a group sees at most P atomics.
+__global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
+  __shared__ float red[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = blockIdx.x, g = blockIdx.y;
+  int64_t r0, r1;
+  if (a.scale_mode == NV4_SCALE_TENSOR) { r0 = 0; r1 = a.rows; }
+  else if (a.seg_offsets) { r0 = a.seg_offsets[g]; r1 = a.seg_offsets[g + 1]; }
+  else { const int64_t len = a.rows / a.nseg; r0 = (int64_t)g * len; r1 = r0 + len; }
   float m = 0.0f;
   bool bad = false;
-  for (int64_t row = wave; row < a.rows; row += nwaves) {
-    int g = row_group(a, row);
-    if (g != cur) {
-      if (cur >= 0) {
-        float w = wave_max(m);
-        if (lane == 0) atomic_max_nonneg(&a.amax_acc[cur], w);
-      }
-      cur = g;
-      m = 0.0f;
-    }
+  for (int64_t row = r0 + (int64_t)p * (kThreads / 64) + wave; row < r1; row += (int64_t)P * (kThreads / 64)) {
     const int64_t base = row * a.ldx;
     for (int64_t k = (int64_t)lane * 8; k < a.K; k += 512) {
       float v[8];
       load8(a.x, a.x_is_f32, base + k, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float av = fabsf(v[i]);
+        const float av = fabsf(v[i]);
         bad |= !(av <= 3.402823466e38f);
         m = fmaxf(m, av);
       }
     }
   }
-  if (cur >= 0) {
-    float w = wave_max(m);
-    if (lane == 0) atomic_max_nonneg(&a.amax_acc[cur], w);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float w = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) w = fmaxf(w, red[i]);
+    atomic_max_nonneg(&a.amax_acc[g], w);
   }
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
@@ -127,6 +127,28 @@ __device__ __forceinline__ uint32_t quant_half_block(const float v[8], float S, 
   return p;
 }
 
+// Same with fp32(S / sf) looked up in a table of the 127 E4M3 values.
+__device__ __forceinline__ uint32_t quant_half_block_tab(const float v[8], float S, const float *inv_tab,
+                                                         uint32_t &sf_out, bool &bad) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float av = fabsf(v[i]);
+    bad |= !(av <= 3.402823466e38f);
+    m = fmaxf(m, av);
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, kWave));
+  const uint32_t sf = e4m3_from_f32(__fmul_rn(__fdiv_rn(m, 6.0f), S));
+  const float inv = inv_tab[sf];
+  uint32_t p = 0;
+  p = pack_e2m1_pair<0>(p, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
+  p = pack_e2m1_pair<1>(p, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
+  p = pack_e2m1_pair<2>(p, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
+  p = pack_e2m1_pair<3>(p, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
+  sf_out = sf;
+  return p;
+}
+
 // Write the decode scales G (and, when the amax came from amax_in, amax_out).
 __device__ void write_group_scales(const QuantArgs &a) {
   const float *A = amax_src(a);
@@ -138,11 +160,20 @@ __device__ void write_group_scales(const QuantArgs &a) {
 }
 
 // Row layout, tensor or segment scales: every lane quantises 8 consecutive
-// elements (16-byte load, 4-byte code store); waves stride over the flat
-// (row, chunk) index so that loads and stores are fully coalesced.
+// elements per chunk (16-byte load, 4-byte code store), two chunks in flight;
+// waves stride over the flat (row, chunk) index so that loads and stores are
+// fully coalesced.  With one tensor scale, fp32(S / sf) comes from an LDS table
+// of the 127 E4M3 values (the same correctly rounded quotients).
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
+  __shared__ float inv_tab[128];
   if (blockIdx.x == 0) write_group_scales(a);
   const float *A = amax_src(a);
+  const bool tensor = a.scale_mode == NV4_SCALE_TENSOR;
+  const float S_tensor = tensor ? tensor_encode_scale(A[0]) : 1.0f;
+  if (tensor) {
+    if (threadIdx.x < 128) inv_tab[threadIdx.x] = threadIdx.x ? __fdiv_rn(S_tensor, e4m3_to_f32(threadIdx.x)) : 0.0f;
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int64_t kc = a.K >> 3;  // 8-element chunks per row (even)
   const int64_t total = a.rows * kc;
@@ -151,20 +182,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
   int cur = -1;
   float S = 1.0f;
   bool bad = false;
-  for (int64_t c0 = wave * 64; c0 < total; c0 += stride) {
-    const int64_t c = c0 + lane;
-    const bool act = c < total;
-    const int64_t cc = act ? c : c0;  // inactive lanes (and their partners) recompute chunk c0
-    const int64_t row = cc / kc, ch = cc - row * kc;
-    const int g = row_group(a, row);
-    if (g != cur) { cur = g; S = tensor_encode_scale(A[g]); }
-    float v[8];
-    load8(a.x, a.x_is_f32, row * a.ldx + ch * 8, v);
-    uint32_t sf;
-    const uint32_t p = quant_half_block(v, S, sf, bad);
-    if (act) {
-      reinterpret_cast<uint32_t *>(a.codes)[row * (a.out_K >> 3) + ch] = p;
-      if ((ch & 1) == 0) a.scales[row * (a.out_K >> 4) + (ch >> 1)] = (uint8_t)sf;
+  for (int64_t c0 = wave * 64; c0 < total; c0 += 2 * stride) {
+    int64_t row[2], ch[2];
+    bool act[2];
+    float v[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t base = c0 + u * stride;
+      const int64_t c = base + lane;
+      act[u] = c < total;
+      const int64_t cc = act[u] ? c : (base < total ? base : c0);  // inactive lanes (and their partners) redo a valid chunk
+      row[u] = cc / kc;
+      ch[u] = cc - row[u] * kc;
+      load8(a.x, a.x_is_f32, row[u] * a.ldx + ch[u] * 8, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t sf, p;
+      if (tensor) {
+        p = quant_half_block_tab(v[u], S_tensor, inv_tab, sf, bad);
+      } else {
+        const int g = row_group(a, row[u]);
+        if (g != cur) { cur = g; S = tensor_encode_scale(A[g]); }
+        p = quant_half_block(v[u], S, sf, bad);
+      }
+      if (act[u]) {
+        reinterpret_cast<uint32_t *>(a.codes)[row[u] * (a.out_K >> 3) + ch[u]] = p;
+        if ((ch[u] & 1) == 0) a.scales[row[u] * (a.out_K >> 4) + (ch[u] >> 1)] = (uint8_t)sf;
+      }
     }
   }
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
@@ -293,8 +338,11 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
   if (!a.amax_in && !per_row) {
     k_fill_zero<<<(a.ngroups + 255) / 256, 256, 0, stream>>>(a.amax_acc, a.ngroups);
     if (a.rows > 0) {
-      const int grid = (int)std::min<int64_t>((a.rows + 3) / 4, (int64_t)cus * 8);
-      k_amax_rows<<<grid, kThreads, 0, stream>>>(a);
+      // about two workgroups per CU in total, split over the groups
+      const int groups = a.scale_mode == NV4_SCALE_TENSOR ? 1 : a.nseg;
+      const int64_t rows_per_group = (a.rows + groups - 1) / groups;
+      const int P = (int)std::max<int64_t>(1, std::min<int64_t>((2 * cus + groups - 1) / groups, (rows_per_group + 3) / 4));
+      k_amax_rows<<<dim3(P, groups), kThreads, 0, stream>>>(a, P);
     }
   }
   if (a.layout == NV4_ROWS) {
@@ -303,7 +351,7 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
       k_quant_rows_per_row<<<grid, kThreads, 0, stream>>>(a);
     } else {
       const int64_t chunks = a.rows * (a.K >> 3);
-      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + kThreads - 1) / kThreads, (int64_t)cus * 16));
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + 2 * kThreads - 1) / (2 * kThreads), (int64_t)cus * 8));
       k_quant_rows<<<grid, kThreads, 0, stream>>>(a);
     }
   } else {
