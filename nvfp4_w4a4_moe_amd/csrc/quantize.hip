@@ -24,21 +24,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ void load8(const void *x, int x_is_f32, int64_t off, float v[8]) {
-  if (x_is_f32) {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
-    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xFFFF0000u);
-    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xFFFF0000u);
-  }
-}
-
 __device__ __forceinline__ float load1(const void *x, int x_is_f32, int64_t off) {
   if (x_is_f32) return static_cast<const float *>(x)[off];
   return bf16_bits_to_f32(static_cast<const uint16_t *>(x)[off]);
@@ -66,11 +51,63 @@ __global__ void k_fill_zero(float *p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Group amax.  Workgroup (p, g) scans rows p, p + P, ... of group g's row range
-// (an equal split of the rows, or [seg_offsets[g], seg_offsets[g+1])); its
+// Raw 8-element chunk (BF16: one 16-byte load; FP32: two).
+template <bool F32>
+struct Chunk {
+  uint4 w[F32 ? 2 : 1];
+};
+
+template <bool F32>
+__device__ __forceinline__ Chunk<F32> load_chunk(const void *x, int64_t off) {
+  Chunk<F32> c;
+  if (F32) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + off);
+    c.w[0] = p[0];
+    c.w[F32 ? 1 : 0] = p[1];
+  } else {
+    c.w[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+  }
+  return c;
+}
+
+template <bool F32>
+__device__ __forceinline__ void unpack_chunk(const Chunk<F32> &c, float v[8]) {
+  if (F32) {
+    v[0] = __uint_as_float(c.w[0].x); v[1] = __uint_as_float(c.w[0].y);
+    v[2] = __uint_as_float(c.w[0].z); v[3] = __uint_as_float(c.w[0].w);
+    v[4] = __uint_as_float(c.w[F32 ? 1 : 0].x); v[5] = __uint_as_float(c.w[F32 ? 1 : 0].y);
+    v[6] = __uint_as_float(c.w[F32 ? 1 : 0].z); v[7] = __uint_as_float(c.w[F32 ? 1 : 0].w);
+  } else {
+    const uint4 u = c.w[0];
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xFFFF0000u);
+  }
+}
+
+// Position (row, chunk) of a lane's 8-element chunk in the flat chunk order of a
+// row range; stepping by a fixed number of chunks needs no division.
+struct Pos {
+  int64_t row, ch;
+};
+
+__device__ __forceinline__ Pos pos_step(Pos p, int64_t dr, int64_t dc, int64_t kc) {
+  p.ch += dc;
+  p.row += dr;
+  if (p.ch >= kc) { p.ch -= kc; p.row += 1; }
+  return p;
+}
+
+// Group amax.  Workgroup (p, g) scans the chunks of group g's row range (an
+// equal split of the rows, or [seg_offsets[g], seg_offsets[g+1])) in flat order,
+// workgroup p taking every P-th run of 256 chunks, eight loads in flight per lane;
 // waves reduce in registers and LDS, and one order-independent atomic max per
-// workgroup goes to amax_acc[g], so a group sees at most P atomics.
+// workgroup goes to amax_acc[g].  Atomics on one address serialise in L2, so P
+// stays near one workgroup per CU in total.
+template <bool F32>
 __global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
+  constexpr int U = 8;
   __shared__ float red[kThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = blockIdx.x, g = blockIdx.y;
@@ -78,16 +115,30 @@ __global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
   if (a.scale_mode == NV4_SCALE_TENSOR) { r0 = 0; r1 = a.rows; }
   else if (a.seg_offsets) { r0 = a.seg_offsets[g]; r1 = a.seg_offsets[g + 1]; }
   else { const int64_t len = a.rows / a.nseg; r0 = (int64_t)g * len; r1 = r0 + len; }
+  const int64_t kc = a.K >> 3;
+  const int64_t total = (r1 - r0) * kc;
+  const int64_t stride = (int64_t)P * kThreads;
+  const int64_t dr = stride / kc, dc = stride % kc;
+  const int64_t c0 = (int64_t)p * kThreads + wave * 64 + lane;
+  Pos pos = {r0 + c0 / kc, c0 % kc};
   float m = 0.0f;
   bool bad = false;
-  for (int64_t row = r0 + (int64_t)p * (kThreads / 64) + wave; row < r1; row += (int64_t)P * (kThreads / 64)) {
-    const int64_t base = row * a.ldx;
-    for (int64_t k = (int64_t)lane * 8; k < a.K; k += 512) {
+  for (int64_t base = (int64_t)p * kThreads + wave * 64; base < total; base += U * stride) {
+    Chunk<F32> c[U];
+    bool act[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      act[u] = base + u * stride + lane < total;
+      c[u] = load_chunk<F32>(a.x, act[u] ? pos.row * a.ldx + pos.ch * 8 : 0);
+      pos = pos_step(pos, dr, dc, kc);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       float v[8];
-      load8(a.x, a.x_is_f32, base + k, v);
+      unpack_chunk<F32>(c[u], v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float av = fabsf(v[i]);
+        const float av = act[u] ? fabsf(v[i]) : 0.0f;
         bad |= !(av <= 3.402823466e38f);
         m = fmaxf(m, av);
       }
@@ -104,42 +155,41 @@ __global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
 
-// Quantise one 8-element half-block held by this lane; the partner lane (lane ^ 1)
-// holds the other half of the same 16-element block.  Returns the packed codes
-// and the block scale byte.
-__device__ __forceinline__ uint32_t quant_half_block(const float v[8], float S, uint32_t &sf_out, bool &bad) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float av = fabsf(v[i]);
-    bad |= !(av <= 3.402823466e38f);
-    m = fmaxf(m, av);
-  }
-  m = fmaxf(m, __shfl_xor(m, 1, kWave));
-  const uint32_t sf = e4m3_from_f32(__fmul_rn(__fdiv_rn(m, 6.0f), S));
-  const float inv = sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f;
-  uint32_t p = 0;
-  p = pack_e2m1_pair<0>(p, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
-  p = pack_e2m1_pair<1>(p, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
-  p = pack_e2m1_pair<2>(p, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
-  p = pack_e2m1_pair<3>(p, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
-  sf_out = sf;
-  return p;
+// fp32(m / 6), correctly rounded.  For m >= 2^-122 the quotient is normal and one
+// Newton correction of m * fp32(1/6) with an exact FMA remainder gives the
+// correctly rounded quotient (Markstein, "Computation of elementary functions on
+// the IBM RISC System/6000 processor", 1990; checked exhaustively over every
+// FP32 m >= 2^-122).  Smaller nonzero m (subnormal quotients) take the division.
+__device__ __forceinline__ float div6_rn(float m) {
+  const float r6 = 0.16666667163372039794921875f;  // fp32(1/6)
+  const float q0 = __fmul_rn(m, r6);
+  const float rem = __builtin_fmaf(-q0, 6.0f, m);
+  float q = __builtin_fmaf(rem, r6, q0);
+  if (m < 0x1p-122f) q = __fdiv_rn(m, 6.0f);
+  return q;
 }
 
-// Same with fp32(S / sf) looked up in a table of the 127 E4M3 values.
-__device__ __forceinline__ uint32_t quant_half_block_tab(const float v[8], float S, const float *inv_tab,
-                                                         uint32_t &sf_out, bool &bad) {
+// value of lane ^ 1 (quad permutation [1, 0, 3, 2] of the data-parallel primitives)
+__device__ __forceinline__ float xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Quantise one 8-element half-block held by this lane; the partner lane (lane ^ 1)
+// holds the other half of the same 16-element block.  With inv_tab, fp32(S / sf)
+// is read from a table of the 127 E4M3 values (the same correctly rounded
+// quotients).  Returns the packed codes and the block scale byte.
+__device__ __forceinline__ uint32_t quant_half_block(const float v[8], float S, const float *inv_tab,
+                                                     uint32_t &sf_out, bool &bad) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float av = fabsf(v[i]);
+    const float av = fabsf(v[i]);
     bad |= !(av <= 3.402823466e38f);
     m = fmaxf(m, av);
   }
-  m = fmaxf(m, __shfl_xor(m, 1, kWave));
-  const uint32_t sf = e4m3_from_f32(__fmul_rn(__fdiv_rn(m, 6.0f), S));
-  const float inv = inv_tab[sf];
+  m = fmaxf(m, xor1(m));
+  const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
+  const float inv = inv_tab ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
   uint32_t p = 0;
   p = pack_e2m1_pair<0>(p, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
   p = pack_e2m1_pair<1>(p, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
@@ -160,56 +210,74 @@ __device__ void write_group_scales(const QuantArgs &a) {
 }
 
 // Row layout, tensor or segment scales: every lane quantises 8 consecutive
-// elements per chunk (16-byte load, 4-byte code store), two chunks in flight;
-// waves stride over the flat (row, chunk) index so that loads and stores are
-// fully coalesced.  With one tensor scale, fp32(S / sf) comes from an LDS table
-// of the 127 E4M3 values (the same correctly rounded quotients).
+// elements per chunk (one 16-byte BF16 load, one 4-byte code store); waves
+// stride over the flat (row, chunk) order so that loads and stores are fully
+// coalesced.  Each iteration quantises two chunks per lane while the loads of
+// the next two are in flight.  The two lanes of a block are always both active
+// or both inactive (K % 16 == 0 and runs start at multiples of 64 chunks).
+// With one tensor scale, fp32(S / sf) comes from an LDS table.
+template <bool F32, bool TENSOR>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
   __shared__ float inv_tab[128];
   if (blockIdx.x == 0) write_group_scales(a);
   const float *A = amax_src(a);
-  const bool tensor = a.scale_mode == NV4_SCALE_TENSOR;
-  const float S_tensor = tensor ? tensor_encode_scale(A[0]) : 1.0f;
-  if (tensor) {
+  const float S_tensor = TENSOR ? tensor_encode_scale(A[0]) : 1.0f;
+  if (TENSOR) {
     if (threadIdx.x < 128) inv_tab[threadIdx.x] = threadIdx.x ? __fdiv_rn(S_tensor, e4m3_to_f32(threadIdx.x)) : 0.0f;
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
   const int64_t kc = a.K >> 3;  // 8-element chunks per row (even)
   const int64_t total = a.rows * kc;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int cur = -1;
-  float S = 1.0f;
+  const int64_t dr = stride / kc, dc = stride % kc;
+  const int64_t w0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 64;
+  uint32_t *codes = reinterpret_cast<uint32_t *>(a.codes);
+  const int64_t cstride = a.out_K >> 3, sstride = a.out_K >> 4;
+  Pos q[2];
+  q[0] = Pos{(w0 + lane) / kc, (w0 + lane) % kc};
+  q[1] = pos_step(q[0], dr, dc, kc);
+  Chunk<F32> cur[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    cur[u] = load_chunk<F32>(a.x, w0 + u * stride + lane < total ? q[u].row * a.ldx + q[u].ch * 8 : 0);
+  int64_t g_lo = 0, g_hi = 0;  // row range of the group whose scale S holds
+  float S = S_tensor;
   bool bad = false;
-  for (int64_t c0 = wave * 64; c0 < total; c0 += 2 * stride) {
-    int64_t row[2], ch[2];
-    bool act[2];
-    float v[2][8];
+  for (int64_t base = w0; base < total; base += 2 * stride) {
+    Pos nq[2];
+    Chunk<F32> nxt[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t base = c0 + u * stride;
-      const int64_t c = base + lane;
-      act[u] = c < total;
-      const int64_t cc = act[u] ? c : (base < total ? base : c0);  // inactive lanes (and their partners) redo a valid chunk
-      row[u] = cc / kc;
-      ch[u] = cc - row[u] * kc;
-      load8(a.x, a.x_is_f32, row[u] * a.ldx + ch[u] * 8, v[u]);
+      nq[u] = pos_step(pos_step(q[u], dr, dc, kc), dr, dc, kc);
+      const bool nact = base + (2 + u) * stride + lane < total;
+      nxt[u] = load_chunk<F32>(a.x, nact ? nq[u].row * a.ldx + nq[u].ch * 8 : 0);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      const bool act = base + u * stride + lane < total;
+      float v[8];
+      unpack_chunk<F32>(cur[u], v);
       uint32_t sf, p;
-      if (tensor) {
-        p = quant_half_block_tab(v[u], S_tensor, inv_tab, sf, bad);
+      if (TENSOR) {
+        p = quant_half_block(v, S_tensor, inv_tab, sf, bad);
       } else {
-        const int g = row_group(a, row[u]);
-        if (g != cur) { cur = g; S = tensor_encode_scale(A[g]); }
-        p = quant_half_block(v[u], S, sf, bad);
+        const int64_t row = act ? q[u].row : 0;
+        if (row < g_lo || row >= g_hi) {  // entered another group: its row range and scale
+          const int g = row_group(a, row);
+          if (a.scale_mode == NV4_SCALE_ROW) { g_lo = row; g_hi = row + 1; }
+          else if (a.seg_offsets) { g_lo = a.seg_offsets[g]; g_hi = a.seg_offsets[g + 1]; }
+          else { g_lo = (int64_t)g * (a.rows / a.nseg); g_hi = g_lo + a.rows / a.nseg; }
+          S = tensor_encode_scale(A[g]);
+        }
+        p = quant_half_block(v, S, nullptr, sf, bad);
       }
-      if (act[u]) {
-        reinterpret_cast<uint32_t *>(a.codes)[row[u] * (a.out_K >> 3) + ch[u]] = p;
-        if ((ch[u] & 1) == 0) a.scales[row[u] * (a.out_K >> 4) + (ch[u] >> 1)] = (uint8_t)sf;
+      if (act) {
+        codes[q[u].row * cstride + q[u].ch] = p;
+        if ((q[u].ch & 1) == 0) a.scales[q[u].row * sstride + (q[u].ch >> 1)] = (uint8_t)sf;
       }
+      q[u] = nq[u];
+      cur[u] = nxt[u];
     }
   }
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
@@ -217,6 +285,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
 
 // Row layout with one scale per row (the per-token variant): one wave per row,
 // amax and quantisation fused (the row is read twice, the second time from cache).
+template <bool F32>
 __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -231,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
       float m = 0.0f;
       for (int64_t k = (int64_t)lane * 8; k < a.K; k += 512) {
         float v[8];
-        load8(a.x, a.x_is_f32, base + k, v);
+        unpack_chunk<F32>(load_chunk<F32>(a.x, base + k), v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
       }
@@ -246,9 +315,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
       const int64_t k = k0 + (int64_t)lane * 8;
       const bool act = k < a.K;
       float v[8];
-      load8(a.x, a.x_is_f32, base + (act ? k : k0), v);
+      unpack_chunk<F32>(load_chunk<F32>(a.x, base + (act ? k : k0)), v);
       uint32_t sf;
-      const uint32_t p = quant_half_block(v, S, sf, bad);
+      const uint32_t p = quant_half_block(v, S, nullptr, sf, bad);
       if (act) {
         reinterpret_cast<uint32_t *>(a.codes)[row * (a.out_K >> 3) + (k >> 3)] = p;
         if (((k >> 3) & 1) == 0) a.scales[row * (a.out_K >> 4) + (k >> 4)] = (uint8_t)sf;
@@ -311,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a) {
       bad |= !(av <= 3.402823466e38f);
       mx = fmaxf(mx, av);
     }
-    const uint32_t sf = e4m3_from_f32(__fmul_rn(__fdiv_rn(mx, 6.0f), S));
+    const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(mx), S));
     const float inv = sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f;
     uint32_t p0 = 0, p1 = 0;
     p0 = pack_e2m1_pair<0>(p0, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
@@ -334,25 +403,36 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a) {
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
   const int cus = device_cu_count();
   const int per_row = a.scale_mode == NV4_SCALE_ROW;
+  const bool f32 = a.x_is_f32 != 0;
   // group amax pass (tensor / segment scales without a supplied amax)
   if (!a.amax_in && !per_row) {
     k_fill_zero<<<(a.ngroups + 255) / 256, 256, 0, stream>>>(a.amax_acc, a.ngroups);
     if (a.rows > 0) {
-      // about two workgroups per CU in total, split over the groups
+      // about one workgroup per CU in total, split over the groups, at most one
+      // per 2048 chunks of a group
       const int groups = a.scale_mode == NV4_SCALE_TENSOR ? 1 : a.nseg;
-      const int64_t rows_per_group = (a.rows + groups - 1) / groups;
-      const int P = (int)std::max<int64_t>(1, std::min<int64_t>((2 * cus + groups - 1) / groups, (rows_per_group + 3) / 4));
-      k_amax_rows<<<dim3(P, groups), kThreads, 0, stream>>>(a, P);
+      const int64_t chunks_per_group = (a.rows + groups - 1) / groups * (a.K >> 3);
+      const int P = (int)std::max<int64_t>(1, std::min<int64_t>(cus / groups, (chunks_per_group + 2047) / 2048));
+      if (f32) k_amax_rows<true><<<dim3(P, groups), kThreads, 0, stream>>>(a, P);
+      else k_amax_rows<false><<<dim3(P, groups), kThreads, 0, stream>>>(a, P);
     }
   }
   if (a.layout == NV4_ROWS) {
     if (per_row) {
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((a.rows + 3) / 4, (int64_t)cus * 16));
-      k_quant_rows_per_row<<<grid, kThreads, 0, stream>>>(a);
+      if (f32) k_quant_rows_per_row<true><<<grid, kThreads, 0, stream>>>(a);
+      else k_quant_rows_per_row<false><<<grid, kThreads, 0, stream>>>(a);
     } else {
       const int64_t chunks = a.rows * (a.K >> 3);
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + 2 * kThreads - 1) / (2 * kThreads), (int64_t)cus * 8));
-      k_quant_rows<<<grid, kThreads, 0, stream>>>(a);
+      const bool tensor = a.scale_mode == NV4_SCALE_TENSOR;
+      if (f32) {
+        if (tensor) k_quant_rows<true, true><<<grid, kThreads, 0, stream>>>(a);
+        else k_quant_rows<true, false><<<grid, kThreads, 0, stream>>>(a);
+      } else {
+        if (tensor) k_quant_rows<false, true><<<grid, kThreads, 0, stream>>>(a);
+        else k_quant_rows<false, false><<<grid, kThreads, 0, stream>>>(a);
+      }
     }
   } else {
     // upper bound of output blocks: rows + 15 per segment, in 16-row blocks
