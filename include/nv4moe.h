@@ -131,6 +131,10 @@ const char *nv4_last_error(void);
  * [LBP] "What W4A4 GEMM Actually Changes" (per-tensor or per-token scaling).
  *
  *   x, xtype, ldx    input [rows][ldx] (element stride ldx >= K), BF16 or FP32.
+ *   row_index        device int32 [rows] or NULL (ROWS and COLS layouts): logical
+ *                    row r is read from row row_index[r] of x (a gather fused into
+ *                    the load, e.g. tokens in expert order through moe_permute's
+ *                    row_token); every index must address a row of x.
  *   layout           NV4_ROWS: out is [rows][K], blocks along K.
  *                    NV4_COLS: out is the transpose [K][Kout] of x, where row
  *                      segment s of x (rows [seg_offsets[s], seg_offsets[s+1]))
@@ -162,11 +166,11 @@ const char *nv4_last_error(void);
  *   ws, ws_bytes     device workspace of at least nvfp4_quantize_workspace().
  * Errors: EINVAL (NULL pointer, bad sizes, out shape mismatch), EALIGN (K % 16,
  * ldx % 8 for BF16 / % 4 for FP32, x not 16-byte aligned), EUNSUPPORTED
- * (SCALE_ROW with a COLS layout), EWORKSPACE, EHIP.
+ * (SCALE_ROW with a COLS layout, row_index with NV4_COLS_BATCHED), EWORKSPACE, EHIP.
  */
 size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_mode, int nseg);
 nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
-                          int layout, int scale_mode, int nseg,
+                          const int32_t *row_index, int layout, int scale_mode, int nseg,
                           const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
                           const float *amax_in, float *amax_out, nv4_tensor *out,
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);

@@ -59,7 +59,7 @@ _SIGS = {
     "nv4_status_string": (ctypes.c_char_p, [_I]),
     "nv4_last_error": (ctypes.c_char_p, []),
     "nvfp4_quantize_workspace": (_SZ, [_I64, _I64, _I, _I, _I]),
-    "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
+    "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                             _P, _SZ, _P, _P]),
     "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
     "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
@@ -139,11 +139,16 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
                    seg_offsets: torch.Tensor | None = None, seg_padded_offsets: torch.Tensor | None = None,
                    amax_in: torch.Tensor | None = None, amax_out: torch.Tensor | None = None,
                    out: NVFP4 | None = None, out_K: int | None = None, ws: torch.Tensor | None = None,
-                   dev_status: torch.Tensor | None = None, stream=None) -> NVFP4:
-    """NVFP4-quantise a 2-D BF16/FP32 tensor (row stride x.stride(0))."""
+                   dev_status: torch.Tensor | None = None, row_index: torch.Tensor | None = None,
+                   stream=None) -> NVFP4:
+    """NVFP4-quantise a 2-D BF16/FP32 tensor (row stride x.stride(0)).  With row_index
+    (int32 [rows]), logical row r is x row row_index[r] (rows = row_index.numel())."""
     lib = load()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, K = x.shape
+    if row_index is not None:
+        assert row_index.dtype == torch.int32 and row_index.is_contiguous()
+        rows = row_index.numel()
     if layout == NV4_ROWS:
         orows, oK = rows, K
     elif layout == NV4_COLS_BATCHED:
@@ -158,7 +163,7 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
         ws = torch.empty(lib.nvfp4_quantize_workspace(rows, K, layout, scale_mode, nseg), dtype=torch.uint8,
                          device=x.device)
     d = out.c()
-    _check(lib.nvfp4_quantize(_ptr(x), _dtype(x), rows, K, x.stride(0), layout, scale_mode, nseg,
+    _check(lib.nvfp4_quantize(_ptr(x), _dtype(x), rows, K, x.stride(0), _ptr(row_index), layout, scale_mode, nseg,
                               _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(amax_in), _ptr(amax_out),
                               ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), _ptr(dev_status),
                               _stream(stream)))
@@ -279,13 +284,13 @@ class ForwardBuffers:
     """Every intermediate of one forward, preallocated so that a timed forward
     enqueues kernels only."""
     xq: NVFP4
+    xamax: torch.Tensor
     xg: NVFP4
     hact: torch.Tensor
     hamax: torch.Tensor
     hq: NVFP4
     y: torch.Tensor
     out: torch.Tensor
-    qws: torch.Tensor
     pws: torch.Tensor
     hq_ws: torch.Tensor
     routing: Routing | None = None
@@ -296,14 +301,13 @@ def alloc_forward(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat
     lib = load()
     R = T * k
     return ForwardBuffers(
-        xq=NVFP4.empty(T, H, 1, device), xg=NVFP4.empty(R, H, 1, device),
+        xq=NVFP4.empty(T, H, 1, device), xamax=torch.zeros((1,), dtype=torch.float32, device=device),
+        xg=NVFP4.empty(R, H, 1, device),
         hact=torch.empty((R, I), dtype=hact_dtype, device=device),
         hamax=torch.zeros((1,), dtype=torch.float32, device=device),
         hq=NVFP4.empty(R, I, 1, device),
         y=torch.empty((R, H), dtype=torch.float32, device=device),
         out=torch.empty((T, H), dtype=out_dtype, device=device),
-        qws=torch.empty(lib.nvfp4_quantize_workspace(T, H, NV4_ROWS, NV4_SCALE_TENSOR, 1), dtype=torch.uint8,
-                        device=device),
         pws=torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device),
         hq_ws=torch.empty(256, dtype=torch.uint8, device=device))
 
@@ -336,7 +340,7 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
     R = T * k
     st = stream if stream is not None else torch.cuda.current_stream()
     with _Stage(stage_events, "quantize_x", st):
-        nvfp4_quantize(x, out=bufs.xq, ws=bufs.qws, stream=stream)
+        nvfp4_quantize(x, out=bufs.xq, amax_out=bufs.xamax, stream=stream)
     with _Stage(stage_events, "route_permute", st):
         if fuse_gather:
             bufs.routing = moe_permute(logits, w.E, k, ws=bufs.pws, stream=stream, out=bufs.routing)
@@ -356,4 +360,107 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
         nvfp4_grouped_gemm(bufs.hq, w.w2, bufs.routing.offsets, w.E, H, M_cap=R, C=bufs.y, stream=stream)
     with _Stage(stage_events, "combine", st):
         moe_combine(bufs.y, bufs.routing.token_row, bufs.routing.topk_w, out=bufs.out, stream=stream)
+    return bufs
+
+
+# ----------------------------------------------------------------------------- backward
+
+@dataclass
+class TransposedWeights:
+    """Expert weights transposed and re-quantised along their new contraction
+    dimension (the operands of the data gradients): W2^T [E*I, H] and
+    W13^T [E*H, 2I], one tensor scale per expert and projection."""
+    w2t: NVFP4
+    w13t: NVFP4
+
+
+def quantize_expert_weights_t(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> TransposedWeights:
+    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> per-expert transposes in NVFP4."""
+    E, I2, H = W13.shape
+    w2t = nvfp4_quantize(W2.reshape(E * H, I2 // 2), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT,
+                         nseg=E, stream=stream)
+    w13t = nvfp4_quantize(W13.reshape(E * I2, H), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT,
+                          nseg=E, stream=stream)
+    return TransposedWeights(w2t, w13t)
+
+
+def cols_capacity(R: int, E: int) -> int:
+    """Column capacity of a segment-transposed operand: R rows, each of E segments
+    padded to 16, rounded up to 64."""
+    return ((R + 15 * E + 63) // 64) * 64
+
+
+@dataclass
+class BackwardBuffers:
+    """Every intermediate and result of one backward (preallocated)."""
+    dy2q: NVFP4
+    dy13q: NVFP4
+    dy2_amax: torch.Tensor
+    dy13_amax: torch.Tensor
+    dhact: torch.Tensor     # [R, I]
+    dxperm: torch.Tensor    # [R, H]
+    dy2c: NVFP4             # [H, Kcap]
+    hc: NVFP4               # [I, Kcap]
+    dy13c: NVFP4            # [2I, Kcap]
+    xc: NVFP4               # [H, Kcap]
+    dw2: torch.Tensor       # [E, H, I]
+    dw13: torch.Tensor      # [E, 2I, H]
+
+
+def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfloat16, wgrad_dtype=torch.float32,
+                   device="cuda") -> BackwardBuffers:
+    R = T * k
+    kc = cols_capacity(R, E)
+    f1 = lambda: torch.zeros((1,), dtype=torch.float32, device=device)
+    return BackwardBuffers(
+        dy2q=NVFP4.empty(R, H, 1, device), dy13q=NVFP4.empty(R, 2 * I, 1, device), dy2_amax=f1(), dy13_amax=f1(),
+        dhact=torch.empty((R, I), dtype=dgrad_dtype, device=device),
+        dxperm=torch.empty((R, H), dtype=dgrad_dtype, device=device),
+        dy2c=NVFP4.empty(H, kc, 1, device), hc=NVFP4.empty(I, kc, 1, device),
+        dy13c=NVFP4.empty(2 * I, kc, 1, device), xc=NVFP4.empty(H, kc, 1, device),
+        dw2=torch.empty((E, H, I), dtype=wgrad_dtype, device=device),
+        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device))
+
+
+def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY2: torch.Tensor,
+                 dY13: torch.Tensor, bufs: BackwardBuffers | None = None, stream=None,
+                 stage_events: list | None = None) -> BackwardBuffers:
+    """The four backward grouped GEMMs of the expert layer, every operand re-quantised
+    to NVFP4 along its new contraction dimension.
+
+    dY2 [R, H] is the gradient of the down projection's output rows and dY13 [R, 2I]
+    that of the gate/up output rows, both in expert (permuted) row order.
+      dHact  = dY2_e . W2_e            (GROUP_M over H)
+      dXperm = dY13_e . W13_e          (GROUP_M over 2I)
+      dW2[e]  = dY2_e^T . Hact_e       (GROUP_K over expert e's tokens)
+      dW13[e] = dY13_e^T . Xperm_e     (GROUP_K; Xperm = X rows in expert order)
+    The tensor scale of each activation and gradient operand is the same for its
+    row and column quantisation (one amax per tensor): the row pass of dY records
+    it, the forward recorded those of X and of the SwiGLU output."""
+    T, H = x.shape
+    rt = fwd.routing
+    E = rt.offsets.numel() - 1
+    R = rt.row_token.numel()
+    k = R // T
+    I = fwd.hact.shape[1]
+    if bufs is None:
+        bufs = alloc_backward(T, H, E, k, I, device=x.device)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    seg = dict(layout=NV4_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets, stream=stream)
+    with _Stage(stage_events, "quantize_dy", st):
+        nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, stream=stream)
+        nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, stream=stream)
+    with _Stage(stage_events, "dgrad", st):
+        nvfp4_grouped_gemm(bufs.dy2q, wt.w2t, rt.offsets, E, I, M_cap=R, C=bufs.dhact, stream=stream)
+        nvfp4_grouped_gemm(bufs.dy13q, wt.w13t, rt.offsets, E, H, M_cap=R, C=bufs.dxperm, stream=stream)
+    with _Stage(stage_events, "quantize_cols", st):
+        nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, **seg)
+        nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
+        nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
+        nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
+    with _Stage(stage_events, "wgrad", st):
+        nvfp4_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
+                           stream=stream)
+        nvfp4_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
+                           stream=stream)
     return bufs

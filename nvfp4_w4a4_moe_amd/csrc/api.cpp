@@ -92,7 +92,7 @@ size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_m
 }
 
 nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
-                          int layout, int scale_mode, int nseg,
+                          const int32_t *row_index, int layout, int scale_mode, int nseg,
                           const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
                           const float *amax_in, float *amax_out, nv4_tensor *out,
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
@@ -105,6 +105,8 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
     return fail(NV4_EINVAL, "nvfp4_quantize: bad scale_mode %d", scale_mode);
   if (scale_mode == NV4_SCALE_ROW && layout != NV4_ROWS)
     return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: per-row scales need the NV4_ROWS layout");
+  if (row_index && layout == NV4_COLS_BATCHED)
+    return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: row_index is not supported with NV4_COLS_BATCHED");
   if (K % 16) return fail(NV4_EALIGN, "nvfp4_quantize: K = %lld is not a multiple of 16", (long long)K);
   if (ldx < K) return fail(NV4_EINVAL, "nvfp4_quantize: ldx < K");
   const int64_t esz = xtype == NV4_F32 ? 4 : 2;
@@ -158,6 +160,7 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
   a.rows = rows;
   a.K = K;
   a.ldx = ldx;
+  a.row_index = row_index;
   a.layout = layout;
   a.scale_mode = scale_mode;
   a.nseg = nseg > 0 ? nseg : 1;

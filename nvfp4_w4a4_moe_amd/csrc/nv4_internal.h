@@ -13,6 +13,7 @@ struct QuantArgs {
   const void *x;
   int x_is_f32;
   int64_t rows, K, ldx;
+  const int32_t *row_index;  // may be null: logical row r reads x row row_index[r]
   int layout;        // NV4_ROWS / NV4_COLS / NV4_COLS_BATCHED
   int scale_mode;    // NV4_SCALE_*
   int nseg;

@@ -42,6 +42,11 @@ __device__ __forceinline__ int row_group(const QuantArgs &a, int64_t row) {
   return lo;
 }
 
+// element offset of logical row `row` of x (through the optional row gather)
+__device__ __forceinline__ int64_t row_off(const QuantArgs &a, int64_t row) {
+  return (a.row_index ? (int64_t)a.row_index[row] : row) * a.ldx;
+}
+
 __device__ __forceinline__ const float *amax_src(const QuantArgs &a) {
   return a.amax_in ? a.amax_in : a.amax_acc;
 }
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       act[u] = base + u * stride + lane < total;
-      c[u] = load_chunk<F32>(a.x, act[u] ? pos.row * a.ldx + pos.ch * 8 : 0);
+      c[u] = load_chunk<F32>(a.x, act[u] ? row_off(a, pos.row) + pos.ch * 8 : 0);
       pos = pos_step(pos, dr, dc, kc);
     }
 #pragma unroll
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
   Chunk<F32> cur[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    cur[u] = load_chunk<F32>(a.x, w0 + u * stride + lane < total ? q[u].row * a.ldx + q[u].ch * 8 : 0);
+    cur[u] = load_chunk<F32>(a.x, w0 + u * stride + lane < total ? row_off(a, q[u].row) + q[u].ch * 8 : 0);
   int64_t g_lo = 0, g_hi = 0;  // row range of the group whose scale S holds
   float S = S_tensor;
   bool bad = false;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
     for (int u = 0; u < 2; ++u) {
       nq[u] = pos_step(pos_step(q[u], dr, dc, kc), dr, dc, kc);
       const bool nact = base + (2 + u) * stride + lane < total;
-      nxt[u] = load_chunk<F32>(a.x, nact ? nq[u].row * a.ldx + nq[u].ch * 8 : 0);
+      nxt[u] = load_chunk<F32>(a.x, nact ? row_off(a, nq[u].row) + nq[u].ch * 8 : 0);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
   bool bad = false;
   for (int64_t row = wave; row < a.rows; row += nwaves) {
-    const int64_t base = row * a.ldx;
+    const int64_t base = row_off(a, row);
     float A;
     if (a.amax_in) {
       A = a.amax_in[row];
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t r = r0 + i;
-      v[i] = (r < rend) ? load1(a.x, a.x_is_f32, r * a.ldx + col) : 0.0f;
+      v[i] = (r < rend) ? load1(a.x, a.x_is_f32, row_off(a, r) + col) : 0.0f;
       const float av = fabsf(v[i]);
       bad |= !(av <= 3.402823466e38f);
       mx = fmaxf(mx, av);

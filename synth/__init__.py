@@ -15,6 +15,8 @@ seeded draws stand in for them.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -23,6 +25,32 @@ import torch
 
 def rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
+
+
+# Large draws are split into chunks of this many elements, chunk i drawn from the
+# stream PCG64([seed, i]) (chunks fill in parallel threads; the values do not
+# depend on the thread count).  Draws of at most one chunk use PCG64(seed).
+CHUNK = 1 << 22
+
+
+def _draw(shape, seed: int, kind: str) -> np.ndarray:
+    n = int(np.prod(shape))
+    if n <= CHUNK:
+        g = rng(seed)
+        return g.standard_normal(shape, dtype=np.float32) if kind == "normal" else g.random(shape, dtype=np.float32)
+    out = np.empty(n, dtype=np.float32)
+
+    def fill(i):
+        g = np.random.Generator(np.random.PCG64([seed, i]))
+        a, b = i * CHUNK, min(n, (i + 1) * CHUNK)
+        if kind == "normal":
+            g.standard_normal(b - a, dtype=np.float32, out=out[a:b])
+        else:
+            g.random(b - a, dtype=np.float32, out=out[a:b])
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range((n + CHUNK - 1) // CHUNK)))
+    return out.reshape(shape)
 
 
 def to_bf16_values(x: np.ndarray) -> np.ndarray:
@@ -72,15 +100,16 @@ SEED_X, SEED_OUTLIER, SEED_WGATE, SEED_WUP, SEED_WDOWN, SEED_LOGITS, SEED_DY2, S
 def activations(T: int, H: int, seed: int, outlier_frac: float = 1e-3, outlier_scale: float = 20.0,
                 outliers: bool = True) -> np.ndarray:
     """N(0, 1) activations; a Bernoulli(outlier_frac) mask multiplies by outlier_scale."""
-    x = rng(seed + SEED_X).standard_normal((T, H), dtype=np.float32)
+    x = _draw((T, H), seed + SEED_X, "normal")
     if outliers:
-        m = rng(seed + SEED_OUTLIER).random((T, H), dtype=np.float32) < outlier_frac
-        x = np.where(m, x * np.float32(outlier_scale), x)
+        m = _draw((T, H), seed + SEED_OUTLIER, "uniform") < outlier_frac
+        x[m] *= np.float32(outlier_scale)
     return to_bf16_values(x)
 
 
 def weights(shape, seed: int, std: float = 0.02) -> np.ndarray:
-    w = rng(seed).standard_normal(shape, dtype=np.float32) * np.float32(std)
+    w = _draw(shape, seed, "normal")
+    w *= np.float32(std)
     return to_bf16_values(w)
 
 

@@ -51,7 +51,8 @@ def test_status_strings(lib):
 def _q(lib, **kw):
     d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, kw.get("orows", 32), kw.get("oK", 64), 0, 1)
     return lib.nvfp4_quantize(ctypes.c_void_p(kw.get("x", 0x1000)), kw.get("xt", 0), kw.get("rows", 32),
-                              kw.get("K", 64), kw.get("ldx", 64), kw.get("layout", 1), kw.get("mode", 0),
+                              kw.get("K", 64), kw.get("ldx", 64), kw.get("row_index"), kw.get("layout", 1),
+                              kw.get("mode", 0),
                               kw.get("nseg", 1), None, None, None, None, ctypes.byref(d),
                               ctypes.c_void_p(0x1000), 1 << 20, None, None)
 
@@ -69,8 +70,10 @@ def test_quantize_validation(lib):
     assert b"multiple of 16" in lib.nv4_last_error()
     # NV4_COLS without segment offsets
     assert _q(lib, layout=2, orows=64, oK=64) == -1
+    # row gather is not offered for the batched transpose
+    assert _q(lib, layout=3, nseg=2, orows=2 * 64, oK=16, row_index=ctypes.c_void_p(0x1000)) == -3
     d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 32, 64, 0, 1)
-    assert lib.nvfp4_quantize(ctypes.c_void_p(0x1000), 0, 32, 64, 64, 1, 0, 1, None, None, None, None,
+    assert lib.nvfp4_quantize(ctypes.c_void_p(0x1000), 0, 32, 64, 64, None, 1, 0, 1, None, None, None, None,
                               ctypes.byref(d), None, 0, None, None) == -4      # no workspace
 
 
