@@ -447,20 +447,26 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
         bufs = alloc_backward(T, H, E, k, I, device=x.device)
     st = stream if stream is not None else torch.cuda.current_stream()
     seg = dict(layout=NV4_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets, stream=stream)
-    with _Stage(stage_events, "quantize_dy", st):
+    with _Stage(stage_events, "quantize_dy2", st):
         nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, stream=stream)
+    with _Stage(stage_events, "quantize_dy13", st):
         nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, stream=stream)
-    with _Stage(stage_events, "dgrad", st):
+    with _Stage(stage_events, "dgrad_hact", st):
         nvfp4_grouped_gemm(bufs.dy2q, wt.w2t, rt.offsets, E, I, M_cap=R, C=bufs.dhact, stream=stream)
+    with _Stage(stage_events, "dgrad_x", st):
         nvfp4_grouped_gemm(bufs.dy13q, wt.w13t, rt.offsets, E, H, M_cap=R, C=bufs.dxperm, stream=stream)
-    with _Stage(stage_events, "quantize_cols", st):
+    with _Stage(stage_events, "quantize_cols_dy2", st):
         nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, **seg)
+    with _Stage(stage_events, "quantize_cols_hact", st):
         nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
-        nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
-        nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
-    with _Stage(stage_events, "wgrad", st):
+    with _Stage(stage_events, "wgrad_w2", st):
         nvfp4_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
                            stream=stream)
+    with _Stage(stage_events, "quantize_cols_dy13", st):
+        nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
+    with _Stage(stage_events, "quantize_cols_x", st):
+        nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
+    with _Stage(stage_events, "wgrad_w13", st):
         nvfp4_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
                            stream=stream)
     return bufs

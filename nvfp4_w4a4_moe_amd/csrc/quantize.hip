@@ -15,6 +15,9 @@
 //
 // Memory: every kernel streams its input once with 16-byte loads (the amax pass
 // is a second read when the group amax is not supplied).
+#include <algorithm>
+#include <type_traits>
+
 #include "nv4_device.h"
 #include "nv4_internal.h"
 #include "../../include/nv4moe.h"
@@ -23,11 +26,6 @@ namespace nv4 {
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ float load1(const void *x, int x_is_f32, int64_t off) {
-  if (x_is_f32) return static_cast<const float *>(x)[off];
-  return bf16_bits_to_f32(static_cast<const uint16_t *>(x)[off]);
-}
 
 // group (tensor-scale index) of a source row
 __device__ __forceinline__ int row_group(const QuantArgs &a, int64_t row) {
@@ -332,73 +330,165 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
 
-// Column layouts (transposed operands of the backward GEMMs).  One thread owns
-// one column `col` of x and 4 consecutive output blocks (64 positions along the
-// new K); each block is 16 consecutive rows of one segment (zero beyond the
-// segment's end).  Reads are coalesced across the threads (consecutive columns);
-// each thread writes 32 code bytes and 4 scale bytes of one output row.
-constexpr int kColBlocks = 4;
+// Column layouts (transposed operands of the backward GEMMs).  Output row `c`
+// (a column of x) holds 16-element blocks along positions p of the new K; block
+// p/16 takes 16 consecutive rows of one segment (zero beyond the segment's end):
+//   NV4_COLS          segment s owns positions [pad[s], pad[s+1]) and rows
+//                     [off[s], off[s+1]); output row c; positions past pad[nseg]
+//                     are not written.
+//   NV4_COLS_BATCHED  matrix s (rows [s*m, (s+1)*m)) -> output rows s*C + c,
+//                     positions [0, m).
+// One workgroup transposes a tile of 256 positions x 64 columns through LDS:
+//   1. 16-byte coalesced loads of the tile's source rows (8 loads per lane in
+//      flight), zero for padding, into LDS [position][column];
+//   2. lane = column, each wave 4 blocks: read 16 values down the column, block
+//      amax, E4M3 scale, 16 E2M1 codes; codes and scales go to an LDS out-tile;
+//   3. coalesced stores: 16 lanes write the 128 code bytes (and 16 scale bytes)
+//      of one output row of the tile.
+constexpr int kColP = 256;          // positions per tile (16 blocks)
+constexpr int kColC = 64;           // columns per tile
+constexpr int kOutPitch = 136;      // LDS out-tile row pitch (bytes), breaks bank aliasing
+constexpr int kScalePitch = 20;
 
-__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a) {
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles_per_seg) {
+  typedef typename std::conditional<F32, float, uint16_t>::type T;
+  constexpr int kVec = 16 / sizeof(T);               // elements per 16-byte load
+  constexpr int kLanesPerRow = kColC / kVec;         // 8 (BF16) or 16 (FP32)
+  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+  constexpr int kPasses = kColP / kRowsPerPass;      // 8 or 16
+  __shared__ __attribute__((aligned(16))) T tile[kColP][kColC];
+  __shared__ __attribute__((aligned(16))) uint8_t ocodes[kColC][kOutPitch];
+  __shared__ uint8_t oscales[kColC][kScalePitch];
+  __shared__ int64_t bsrc[16];
+  __shared__ int bnum[16], bgrp[16];
+  __shared__ float inv_tab[128];
+
   if (blockIdx.x == 0 && blockIdx.y == 0) write_group_scales(a);
   const float *A = amax_src(a);
   const int64_t C = a.K;  // columns of x
-  const int64_t col = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColC;
   const bool batched = a.layout == NV4_COLS_BATCHED;
-  const int64_t m = batched ? a.rows / a.nseg : 0;
-  const int64_t nblk_total = batched ? (a.rows >> 4) : (int64_t)(a.seg_padded_offsets[a.nseg] >> 4);
-  const int64_t b0 = (int64_t)blockIdx.y * kColBlocks;
-  if (b0 >= nblk_total || col >= C) return;
-  bool bad = false;
-  for (int bi = 0; bi < kColBlocks; ++bi) {
-    const int64_t b = b0 + bi;
-    if (b >= nblk_total) break;
-    int s;
-    int64_t r0, rend, out_row, out_pos;
-    if (batched) {
-      s = (int)(b / (m >> 4));
-      r0 = (int64_t)s * m + (b * 16 - (int64_t)s * m);
-      rend = (int64_t)(s + 1) * m;
-      out_row = (int64_t)s * C + col;
-      out_pos = b * 16 - (int64_t)s * m;
-    } else {
-      int lo = 0, hi = a.nseg - 1;  // segment whose padded range holds position b*16
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (a.seg_padded_offsets[mid] <= b * 16) lo = mid; else hi = mid - 1;
+  int s_tile = 0;
+  int64_t p0, plimit, orow0;
+  if (batched) {
+    s_tile = blockIdx.y / ptiles_per_seg;
+    p0 = (int64_t)(blockIdx.y % ptiles_per_seg) * kColP;
+    plimit = a.rows / a.nseg;
+    orow0 = (int64_t)s_tile * C + c0;
+  } else {
+    p0 = (int64_t)blockIdx.y * kColP;
+    plimit = a.seg_padded_offsets[a.nseg];
+    orow0 = c0;
+  }
+  if (p0 >= plimit) return;  // uniform over the workgroup
+  const bool seg_scales = a.scale_mode == NV4_SCALE_SEGMENT;
+  // per-block source rows: start, count (0..16), scale group
+  if (threadIdx.x < 16) {
+    const int j = threadIdx.x;
+    const int64_t p = p0 + 16 * j;
+    int64_t start = 0;
+    int n = 0, g = 0;
+    if (p < plimit) {
+      if (batched) {
+        start = (int64_t)s_tile * plimit + p;
+        n = 16;
+        g = seg_scales ? s_tile : 0;
+      } else {
+        int lo = 0, hi = a.nseg - 1;  // last segment s with pad[s] <= p
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (a.seg_padded_offsets[mid] <= p) lo = mid; else hi = mid - 1;
+        }
+        start = a.seg_offsets[lo] + (p - a.seg_padded_offsets[lo]);
+        n = (int)std::min<int64_t>(16, std::max<int64_t>(0, a.seg_offsets[lo + 1] - start));
+        g = seg_scales ? lo : 0;
       }
-      s = lo;
-      r0 = a.seg_offsets[s] + (b * 16 - a.seg_padded_offsets[s]);
-      rend = a.seg_offsets[s + 1];
-      out_row = col;
-      out_pos = b * 16;
     }
-    const int g = a.scale_mode == NV4_SCALE_TENSOR ? 0 : s;
-    const float S = tensor_encode_scale(A[g]);
-    float v[16];
-    float mx = 0.0f;
+    bsrc[j] = start;
+    bnum[j] = n;
+    bgrp[j] = g;
+  }
+  // one tensor scale for the whole tile: 1 / block scale from a table
+  const bool uniform = !seg_scales || batched;
+  const float S_tile = tensor_encode_scale(A[uniform ? (seg_scales ? s_tile : 0) : 0]);
+  if (uniform && threadIdx.x < 128)
+    inv_tab[threadIdx.x] = threadIdx.x ? __fdiv_rn(S_tile, e4m3_to_f32(threadIdx.x)) : 0.0f;
+  __syncthreads();
+
+  // 1. load the tile
+  {
+    const int lr = threadIdx.x / kLanesPerRow, lc = (threadIdx.x % kLanesPerRow) * kVec;
+    const bool col_ok = c0 + lc < C;
+    uint4 v[kPasses];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t r = r0 + i;
-      v[i] = (r < rend) ? load1(a.x, a.x_is_f32, row_off(a, r) + col) : 0.0f;
-      const float av = fabsf(v[i]);
-      bad |= !(av <= 3.402823466e38f);
-      mx = fmaxf(mx, av);
+    for (int i = 0; i < kPasses; ++i) {
+      const int pp = i * kRowsPerPass + lr;
+      const int j = pp >> 4, r = pp & 15;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (col_ok && r < bnum[j]) {
+        const int64_t src = bsrc[j] + r;
+        const T *px = static_cast<const T *>(a.x) + row_off(a, src) + c0 + lc;
+        v[i] = *reinterpret_cast<const uint4 *>(px);
+      }
     }
-    const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(mx), S));
-    const float inv = sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f;
-    uint32_t p0 = 0, p1 = 0;
-    p0 = pack_e2m1_pair<0>(p0, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
-    p0 = pack_e2m1_pair<1>(p0, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
-    p0 = pack_e2m1_pair<2>(p0, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
-    p0 = pack_e2m1_pair<3>(p0, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
-    p1 = pack_e2m1_pair<0>(p1, __fmul_rn(v[8], inv), __fmul_rn(v[9], inv));
-    p1 = pack_e2m1_pair<1>(p1, __fmul_rn(v[10], inv), __fmul_rn(v[11], inv));
-    p1 = pack_e2m1_pair<2>(p1, __fmul_rn(v[12], inv), __fmul_rn(v[13], inv));
-    p1 = pack_e2m1_pair<3>(p1, __fmul_rn(v[14], inv), __fmul_rn(v[15], inv));
-    uint2 *dst = reinterpret_cast<uint2 *>(a.codes + out_row * (a.out_K >> 1) + (out_pos >> 1));
-    *dst = make_uint2(p0, p1);
-    a.scales[out_row * (a.out_K >> 4) + (out_pos >> 4)] = (uint8_t)sf;
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i)
+      *reinterpret_cast<uint4 *>(&tile[i * kRowsPerPass + lr][lc]) = v[i];
+  }
+  __syncthreads();
+
+  // 2. quantise: lane = column, wave w = blocks 4w .. 4w+3
+  bool bad = false;
+  {
+    const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = w * 4 + jj;
+      float v[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const T t = tile[16 * j + i][c];
+        v[i] = F32 ? (float)t : __uint_as_float((uint32_t)t << 16);
+        const float av = fabsf(v[i]);
+        bad |= !(av <= 3.402823466e38f);
+        m = fmaxf(m, av);
+      }
+      float S = S_tile;
+      if (!uniform) S = tensor_encode_scale(A[bgrp[j]]);
+      const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
+      const float inv = uniform ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
+      uint32_t lo = 0, hi = 0;
+      lo = pack_e2m1_pair<0>(lo, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
+      lo = pack_e2m1_pair<1>(lo, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
+      lo = pack_e2m1_pair<2>(lo, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
+      lo = pack_e2m1_pair<3>(lo, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
+      hi = pack_e2m1_pair<0>(hi, __fmul_rn(v[8], inv), __fmul_rn(v[9], inv));
+      hi = pack_e2m1_pair<1>(hi, __fmul_rn(v[10], inv), __fmul_rn(v[11], inv));
+      hi = pack_e2m1_pair<2>(hi, __fmul_rn(v[12], inv), __fmul_rn(v[13], inv));
+      hi = pack_e2m1_pair<3>(hi, __fmul_rn(v[14], inv), __fmul_rn(v[15], inv));
+      *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(lo, hi);
+      oscales[c][j] = (uint8_t)sf;
+    }
+  }
+  __syncthreads();
+
+  // 3. coalesced stores: 16 lanes per output row, one block (8 code bytes) each
+  {
+    const int j = threadIdx.x & 15, rr = threadIdx.x >> 4;
+    const bool blk_ok = p0 + 16 * j < plimit;
+    const int64_t cstride = a.out_K >> 1, sstride = a.out_K >> 4;
+#pragma unroll
+    for (int pass = 0; pass < kColC / 16; ++pass) {
+      const int c = pass * 16 + rr;
+      if (blk_ok && c0 + c < C) {
+        const int64_t orow = orow0 + c;
+        *reinterpret_cast<uint2 *>(a.codes + orow * cstride + (p0 >> 1) + 8 * j) =
+            *reinterpret_cast<const uint2 *>(&ocodes[c][8 * j]);
+        a.scales[orow * sstride + (p0 >> 4) + j] = oscales[c][j];
+      }
+    }
   }
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
@@ -440,10 +530,20 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
       }
     }
   } else {
-    // upper bound of output blocks: rows + 15 per segment, in 16-row blocks
-    const int64_t nblk = a.layout == NV4_COLS_BATCHED ? (a.rows >> 4) : ((a.rows + 15 * (int64_t)a.nseg) >> 4) + 1;
-    dim3 grid((unsigned)((a.K + kThreads - 1) / kThreads), (unsigned)std::max<int64_t>(1, (nblk + kColBlocks - 1) / kColBlocks));
-    k_quant_cols<<<grid, kThreads, 0, stream>>>(a);
+    // tiles of 256 positions x 64 columns; NV4_COLS: an upper bound of the padded
+    // positions (rows + 15 per segment), tiles past the actual end exit at once
+    const unsigned gx = (unsigned)std::max<int64_t>(1, (a.K + kColC - 1) / kColC);
+    int ptiles;
+    unsigned gy;
+    if (a.layout == NV4_COLS_BATCHED) {
+      ptiles = (int)((a.rows / a.nseg + kColP - 1) / kColP);
+      gy = (unsigned)(ptiles * a.nseg);
+    } else {
+      ptiles = 0;
+      gy = (unsigned)std::max<int64_t>(1, (a.rows + 15 * (int64_t)a.nseg + kColP - 1) / kColP);
+    }
+    if (f32) k_quant_cols<true><<<dim3(gx, gy), kThreads, 0, stream>>>(a, ptiles);
+    else k_quant_cols<false><<<dim3(gx, gy), kThreads, 0, stream>>>(a, ptiles);
   }
   return hipGetLastError();
 }
