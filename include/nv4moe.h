@@ -235,8 +235,10 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
  *   C [E][N][ldc] (ldc >= M) gets A_e . B_e^T; an empty range gives zeros.
  *   Tensor scales per tensor.
  *   offsets    device int32 [E+1].
- * Errors: EINVAL, EALIGN (K % 16, A->K != B->K), EUNSUPPORTED (SWIGLU with
- * GROUP_K, row scales with GROUP_K), EWORKSPACE, EHIP.
+ * K (A->K == B->K) must be a positive multiple of 64: the kernel stages K in
+ * 128-wide slices and reads 64-element halves; GROUP_K ranges only need 16.
+ * Errors: EINVAL, EALIGN (K not a positive multiple of 64, A->K != B->K),
+ * EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K), EWORKSPACE, EHIP.
  */
 size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K);
 nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
