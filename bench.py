@@ -71,6 +71,27 @@ def hbm_bytes(cfg) -> dict:
     }
 
 
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the same counters of a plain copy), or None
+    when there is none or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in vals.get("sources", "").split():
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if not vals.get("sources") or h.hexdigest() != vals.get("sources_sha256"):
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride: int = 16,
                  max_experts: int = 3, max_rows: int = 8192) -> dict:
     """The oracle on a bounded sample of the same workload, scaled to one step.
@@ -156,6 +177,9 @@ def main():
     ap.add_argument("--config", default="learner_64k")
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (three times): the known-size kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the GEMM's traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the expert path is built and timed on a single MI355X "
@@ -164,6 +188,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+        return
 
     import nvfp4_w4a4_moe_amd as nv4
     import synth
@@ -269,7 +303,8 @@ def main():
         "weight_quantize_ms": round(float(np.median(wq_ms)), 4),
         "roofline": {"bound": "mfma", "kernel": gemm[dom][1], "stage": dom,
                      "achieved": round(gemm[dom][0], 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm[dom][0] / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None},
+                     "frac": round(gemm[dom][0] / PEAK_F16_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(dom, cfg.name)},
         "other_kernels": other,
     }
     if not args.no_cpu_baseline:
