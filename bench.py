@@ -10,9 +10,10 @@ BF16 inputs and upstream gradients.
 A step is the whole expert path, forward and backward, with every input resident
 in HBM: quantise X (amax + quantise), route + permute, grouped GEMM gate/up +
 SwiGLU (+ amax), quantise the SwiGLU output, grouped GEMM down, combine; then
-quantise the upstream gradients along their rows, the two data-gradient grouped
-GEMMs, the four token-direction (per expert segment) transposed quantisations
-and the two weight-gradient grouped GEMMs.  Expert-weight quantisation (the
+quantise each upstream gradient along its rows and, in the same pass, along its
+tokens per expert segment; the two data-gradient grouped GEMMs; the
+token-direction quantisations of the SwiGLU output and of X (gathered into
+expert order); the two weight-gradient grouped GEMMs.  Expert-weight quantisation (the
 weights and their per-expert transposes) happens once per optimizer step and is
 timed and reported separately.  `--forward-only` times the forward alone.
 
@@ -58,12 +59,14 @@ def hbm_bytes(cfg) -> dict:
     q1 = 2 + 0.5 + 1 / 16           # one-pass quantiser, per element
     kc = ((R + 15 * E + 63) // 64) * 64
     cols = lambda C: R * C * 2 + C * kc * (0.5 + 1 / 16)
+    # upstream gradients: amax pass + one pass writing the row and the column operands
+    dual = lambda C: R * C * (2 + 2 + 0.5 + 1 / 16) + C * kc * (0.5 + 1 / 16)
     return {
         "quantize_x": T * H * (2 + q1),                      # amax pass + one pass
         "quantize_hact": R * I * q1,
         "combine": T * (k * H * 4 + k * 8 + H * 2),
-        "quantize_dy2": R * H * (2 + q1),
-        "quantize_dy13": R * 2 * I * (2 + q1),
+        "quantize_dy2": dual(H),
+        "quantize_dy13": dual(2 * I),
         "quantize_cols_dy2": cols(H),
         "quantize_cols_hact": cols(I),
         "quantize_cols_dy13": cols(2 * I),

@@ -75,6 +75,7 @@ typedef enum nv4_dtype { NV4_BF16 = 0, NV4_F32 = 1 } nv4_dtype;
 #define NV4_ROWS 1          /* blocks of 16 along the contiguous dimension K */
 #define NV4_COLS 2          /* transpose: blocks of 16 down the rows of each segment */
 #define NV4_COLS_BATCHED 3  /* transpose each of nseg equal row-slices separately */
+#define NV4_ROWS_AND_COLS 4 /* NV4_COLS into out and NV4_ROWS into out_rows, one read of x */
 
 /* tensor-scale grouping (nvfp4_quantize `scale_mode`, nv4_tensor.scale_mode) */
 #define NV4_SCALE_TENSOR 0  /* one G for the whole tensor */
@@ -143,6 +144,11 @@ const char *nv4_last_error(void);
  *                      multiple of 16 (padding is written as code 0 / scale 0).
  *                      out->K is the column capacity: >= rows + 15 * nseg, % 16.
  *                      Used for the re-quantised operands of the weight gradients.
+ *                    NV4_ROWS_AND_COLS: both NV4_COLS (into out) and NV4_ROWS
+ *                      (into out_rows) from one read of x, with one tensor scale
+ *                      (SCALE_TENSOR only, K % 64 == 0).  Used for an upstream
+ *                      gradient, which feeds a data gradient (along its rows) and
+ *                      a weight gradient (along its tokens).
  *                    NV4_COLS_BATCHED: x is nseg equal matrices of rows/nseg rows
  *                      (rows/nseg % 16 == 0); out is [nseg*K][rows/nseg], matrix s
  *                      transposed into out rows [s*K, (s+1)*K).  Used for the
@@ -163,16 +169,19 @@ const char *nv4_last_error(void);
  *                    allocated: codes, scales, tscale (ngroups floats) and the
  *                    expected output shape in rows/K.  The library sets
  *                    out->scale_mode and out->nseg.
+ *   out_rows         NV4_ROWS_AND_COLS only (NULL otherwise): descriptor of the
+ *                    row-direction output [rows][K], as `out` for NV4_ROWS.
  *   ws, ws_bytes     device workspace of at least nvfp4_quantize_workspace().
  * Errors: EINVAL (NULL pointer, bad sizes, out shape mismatch), EALIGN (K % 16,
  * ldx % 8 for BF16 / % 4 for FP32, x not 16-byte aligned), EUNSUPPORTED
- * (SCALE_ROW with a COLS layout, row_index with NV4_COLS_BATCHED), EWORKSPACE, EHIP.
+ * (SCALE_ROW with a COLS layout, row_index with NV4_COLS_BATCHED, ROWS_AND_COLS
+ * without SCALE_TENSOR), EWORKSPACE, EHIP.
  */
 size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_mode, int nseg);
 nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
                           const int32_t *row_index, int layout, int scale_mode, int nseg,
                           const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
-                          const float *amax_in, float *amax_out, nv4_tensor *out,
+                          const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libnv4moe.so")
 
 # constants (mirror include/nv4moe.h)
 NV4_BF16, NV4_F32 = 0, 1
-NV4_ROWS, NV4_COLS, NV4_COLS_BATCHED = 1, 2, 3
+NV4_ROWS, NV4_COLS, NV4_COLS_BATCHED, NV4_ROWS_AND_COLS = 1, 2, 3, 4
 NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT, NV4_SCALE_ROW = 0, 1, 2
 NV4_GROUP_M, NV4_GROUP_K = 0, 1
 NV4_EPI_NONE, NV4_EPI_SWIGLU = 0, 1
@@ -60,7 +60,7 @@ _SIGS = {
     "nv4_last_error": (ctypes.c_char_p, []),
     "nvfp4_quantize_workspace": (_SZ, [_I64, _I64, _I, _I, _I]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
-                            _P, _SZ, _P, _P]),
+                            ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
     "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
     "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                          ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
@@ -140,9 +140,11 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
                    amax_in: torch.Tensor | None = None, amax_out: torch.Tensor | None = None,
                    out: NVFP4 | None = None, out_K: int | None = None, ws: torch.Tensor | None = None,
                    dev_status: torch.Tensor | None = None, row_index: torch.Tensor | None = None,
-                   stream=None) -> NVFP4:
+                   out_rows: NVFP4 | None = None, stream=None) -> NVFP4:
     """NVFP4-quantise a 2-D BF16/FP32 tensor (row stride x.stride(0)).  With row_index
-    (int32 [rows]), logical row r is x row row_index[r] (rows = row_index.numel())."""
+    (int32 [rows]), logical row r is x row row_index[r] (rows = row_index.numel()).
+    NV4_ROWS_AND_COLS returns the column output and fills `out_rows` (allocated when
+    None and then reachable as the result's `rows_out` attribute)."""
     lib = load()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, K = x.shape
@@ -156,6 +158,8 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
     else:
         orows = K
         oK = out_K if out_K is not None else ((rows + 15 * nseg + 63) // 64) * 64
+    if layout == NV4_ROWS_AND_COLS and out_rows is None:
+        out_rows = NVFP4.empty(rows, K, 1, device=x.device)
     ng = _ngroups(rows, scale_mode, nseg)
     if out is None:
         out = NVFP4.empty(orows, oK, ng, device=x.device)
@@ -163,11 +167,15 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
         ws = torch.empty(lib.nvfp4_quantize_workspace(rows, K, layout, scale_mode, nseg), dtype=torch.uint8,
                          device=x.device)
     d = out.c()
+    d2 = out_rows.c() if out_rows is not None else None
     _check(lib.nvfp4_quantize(_ptr(x), _dtype(x), rows, K, x.stride(0), _ptr(row_index), layout, scale_mode, nseg,
                               _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(amax_in), _ptr(amax_out),
-                              ctypes.byref(d), _ptr(ws), 0 if ws is None else ws.numel(), _ptr(dev_status),
-                              _stream(stream)))
+                              ctypes.byref(d), None if d2 is None else ctypes.byref(d2), _ptr(ws),
+                              0 if ws is None else ws.numel(), _ptr(dev_status), _stream(stream)))
     out.scale_mode, out.nseg = d.scale_mode, d.nseg
+    if d2 is not None:
+        out_rows.scale_mode, out_rows.nseg = d2.scale_mode, d2.nseg
+        out.rows_out = out_rows
     return out
 
 
@@ -424,7 +432,7 @@ def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfl
 
 def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY2: torch.Tensor,
                  dY13: torch.Tensor, bufs: BackwardBuffers | None = None, stream=None,
-                 stage_events: list | None = None) -> BackwardBuffers:
+                 stage_events: list | None = None, dual: bool = True) -> BackwardBuffers:
     """The four backward grouped GEMMs of the expert layer, every operand re-quantised
     to NVFP4 along its new contraction dimension.
 
@@ -436,7 +444,9 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
       dW13[e] = dY13_e^T . Xperm_e     (GROUP_K; Xperm = X rows in expert order)
     The tensor scale of each activation and gradient operand is the same for its
     row and column quantisation (one amax per tensor): the row pass of dY records
-    it, the forward recorded those of X and of the SwiGLU output."""
+    it, the forward recorded those of X and of the SwiGLU output.  With `dual`, each
+    upstream gradient is read once for both its row and its column quantisation
+    (NV4_ROWS_AND_COLS); otherwise the two are separate passes."""
     T, H = x.shape
     rt = fwd.routing
     E = rt.offsets.numel() - 1
@@ -447,23 +457,33 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
         bufs = alloc_backward(T, H, E, k, I, device=x.device)
     st = stream if stream is not None else torch.cuda.current_stream()
     seg = dict(layout=NV4_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets, stream=stream)
-    with _Stage(stage_events, "quantize_dy2", st):
-        nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, stream=stream)
-    with _Stage(stage_events, "quantize_dy13", st):
-        nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, stream=stream)
+    if dual:
+        both = dict(layout=NV4_ROWS_AND_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets,
+                    stream=stream)
+        with _Stage(stage_events, "quantize_dy2", st):
+            nvfp4_quantize(dY2, out=bufs.dy2c, out_rows=bufs.dy2q, amax_out=bufs.dy2_amax, **both)
+        with _Stage(stage_events, "quantize_dy13", st):
+            nvfp4_quantize(dY13, out=bufs.dy13c, out_rows=bufs.dy13q, amax_out=bufs.dy13_amax, **both)
+    else:
+        with _Stage(stage_events, "quantize_dy2", st):
+            nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, stream=stream)
+        with _Stage(stage_events, "quantize_dy13", st):
+            nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, stream=stream)
     with _Stage(stage_events, "dgrad_hact", st):
         nvfp4_grouped_gemm(bufs.dy2q, wt.w2t, rt.offsets, E, I, M_cap=R, C=bufs.dhact, stream=stream)
     with _Stage(stage_events, "dgrad_x", st):
         nvfp4_grouped_gemm(bufs.dy13q, wt.w13t, rt.offsets, E, H, M_cap=R, C=bufs.dxperm, stream=stream)
-    with _Stage(stage_events, "quantize_cols_dy2", st):
-        nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, **seg)
+    if not dual:
+        with _Stage(stage_events, "quantize_cols_dy2", st):
+            nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, **seg)
     with _Stage(stage_events, "quantize_cols_hact", st):
         nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
     with _Stage(stage_events, "wgrad_w2", st):
         nvfp4_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
                            stream=stream)
-    with _Stage(stage_events, "quantize_cols_dy13", st):
-        nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
+    if not dual:
+        with _Stage(stage_events, "quantize_cols_dy13", st):
+            nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
     with _Stage(stage_events, "quantize_cols_x", st):
         nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
     with _Stage(stage_events, "wgrad_w13", st):

@@ -94,13 +94,25 @@ size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_m
 nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
                           const int32_t *row_index, int layout, int scale_mode, int nseg,
                           const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
-                          const float *amax_in, float *amax_out, nv4_tensor *out,
+                          const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
   if (!out) return fail(NV4_EINVAL, "nvfp4_quantize: out descriptor is NULL");
   if (rows < 0 || K < 0) return fail(NV4_EINVAL, "nvfp4_quantize: negative shape");
   if (xtype != NV4_BF16 && xtype != NV4_F32) return fail(NV4_EINVAL, "nvfp4_quantize: bad input dtype");
-  if (layout != NV4_ROWS && layout != NV4_COLS && layout != NV4_COLS_BATCHED)
+  if (layout != NV4_ROWS && layout != NV4_COLS && layout != NV4_COLS_BATCHED && layout != NV4_ROWS_AND_COLS)
     return fail(NV4_EINVAL, "nvfp4_quantize: bad layout %d", layout);
+  const bool both = layout == NV4_ROWS_AND_COLS;
+  if (both) {
+    if (scale_mode != NV4_SCALE_TENSOR)
+      return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: NV4_ROWS_AND_COLS needs one tensor scale");
+    if (!out_rows || !out_rows->codes || !out_rows->scales || !out_rows->tscale)
+      return fail(NV4_EINVAL, "nvfp4_quantize: NV4_ROWS_AND_COLS needs out_rows");
+    if (K % 64) return fail(NV4_EALIGN, "nvfp4_quantize: NV4_ROWS_AND_COLS needs K %% 64 == 0");
+    if (out_rows->rows != rows || out_rows->K != K)
+      return fail(NV4_EINVAL, "nvfp4_quantize: out_rows must be [rows][K]");
+    if (!aligned(out_rows->codes, 16) || !aligned(out_rows->scales, 4))
+      return fail(NV4_EALIGN, "nvfp4_quantize: out_rows codes must be 16-byte and scales 4-byte aligned");
+  }
   if (scale_mode != NV4_SCALE_TENSOR && scale_mode != NV4_SCALE_SEGMENT && scale_mode != NV4_SCALE_ROW)
     return fail(NV4_EINVAL, "nvfp4_quantize: bad scale_mode %d", scale_mode);
   if (scale_mode == NV4_SCALE_ROW && layout != NV4_ROWS)
@@ -115,7 +127,7 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
   const bool seg_layout = layout != NV4_ROWS;
   if ((scale_mode == NV4_SCALE_SEGMENT || seg_layout) && nseg <= 0)
     return fail(NV4_EINVAL, "nvfp4_quantize: nseg must be positive");
-  if (layout == NV4_COLS && (!seg_offsets || !seg_padded_offsets))
+  if ((layout == NV4_COLS || both) && (!seg_offsets || !seg_padded_offsets))
     return fail(NV4_EINVAL, "nvfp4_quantize: NV4_COLS needs seg_offsets and seg_padded_offsets");
   if (layout == NV4_COLS_BATCHED && (rows % nseg || (rows / nseg) % 16))
     return fail(NV4_EALIGN, "nvfp4_quantize: NV4_COLS_BATCHED needs rows/nseg to be a multiple of 16");
@@ -125,20 +137,20 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
   if (layout == NV4_COLS && scale_mode == NV4_SCALE_SEGMENT && !seg_offsets)
     return fail(NV4_EINVAL, "nvfp4_quantize: segment scales need seg_offsets");
   if (rows >= (1ll << 31) || K >= (1ll << 31)) return fail(NV4_EINVAL, "nvfp4_quantize: shape too large");
-  int64_t out_rows, out_K;
-  if (layout == NV4_ROWS) { out_rows = rows; out_K = K; }
-  else if (layout == NV4_COLS_BATCHED) { out_rows = (int64_t)nseg * K; out_K = rows / nseg; }
-  else { out_rows = K; out_K = out->K; }
-  if (out->rows != out_rows) return fail(NV4_EINVAL, "nvfp4_quantize: out->rows = %lld, expected %lld",
-                                         (long long)out->rows, (long long)out_rows);
-  if (layout == NV4_COLS) {
+  int64_t o_rows, o_K;
+  if (layout == NV4_ROWS) { o_rows = rows; o_K = K; }
+  else if (layout == NV4_COLS_BATCHED) { o_rows = (int64_t)nseg * K; o_K = rows / nseg; }
+  else { o_rows = K; o_K = out->K; }
+  if (out->rows != o_rows) return fail(NV4_EINVAL, "nvfp4_quantize: out->rows = %lld, expected %lld",
+                                         (long long)out->rows, (long long)o_rows);
+  if (layout == NV4_COLS || both) {
     if (out->K % 64) return fail(NV4_EALIGN, "nvfp4_quantize: NV4_COLS needs out->K %% 64 == 0");
     if (out->K < rows + 15 * (int64_t)nseg)
       return fail(NV4_EINVAL, "nvfp4_quantize: out->K must be >= rows + 15 * nseg (padded capacity)");
-  } else if (out->K != out_K) {
-    return fail(NV4_EINVAL, "nvfp4_quantize: out->K = %lld, expected %lld", (long long)out->K, (long long)out_K);
+  } else if (out->K != o_K) {
+    return fail(NV4_EINVAL, "nvfp4_quantize: out->K = %lld, expected %lld", (long long)out->K, (long long)o_K);
   }
-  if (out_rows * out_K >= (1ll << 32)) return fail(NV4_EINVAL, "nvfp4_quantize: output too large");
+  if (o_rows * o_K >= (1ll << 32)) return fail(NV4_EINVAL, "nvfp4_quantize: output too large");
   if ((rows > 0 && K > 0) && (!x || !out->codes || !out->scales))
     return fail(NV4_EINVAL, "nvfp4_quantize: NULL data pointer");
   if (!out->tscale) return fail(NV4_EINVAL, "nvfp4_quantize: out->tscale is NULL");
@@ -171,8 +183,15 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
   a.codes = out->codes;
   a.scales = out->scales;
   a.tscale = out->tscale;
-  a.out_rows = out_rows;
-  a.out_K = layout == NV4_COLS ? out->K : out_K;
+  if (both) {
+    a.codes2 = out_rows->codes;
+    a.scales2 = out_rows->scales;
+    a.tscale2 = out_rows->tscale;
+    out_rows->scale_mode = NV4_SCALE_TENSOR;
+    out_rows->nseg = 1;
+  }
+  a.out_rows = o_rows;
+  a.out_K = (layout == NV4_COLS || both) ? out->K : o_K;
   a.dev_status = dev_status;
   a.ngroups = ng;
   return from_hip(nv4::launch_quantize(a, static_cast<hipStream_t>(stream)), "nvfp4_quantize");

@@ -25,6 +25,8 @@ struct QuantArgs {
   uint8_t *scales;
   float *tscale;
   int64_t out_rows, out_K;            // output tensor shape (codes row stride out_K/2)
+  uint8_t *codes2, *scales2;          // NV4_ROWS_AND_COLS: the row-direction output [rows][K]
+  float *tscale2;
   int32_t *dev_status;
   int ngroups;
 };

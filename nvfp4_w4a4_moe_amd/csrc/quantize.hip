@@ -208,6 +208,7 @@ __device__ void write_group_scales(const QuantArgs &a) {
   for (int g = threadIdx.x; g < a.ngroups; g += blockDim.x) {
     float S = tensor_encode_scale(A[g]);
     a.tscale[g] = __fdiv_rn(1.0f, S);
+    if (a.tscale2) a.tscale2[g] = __fdiv_rn(1.0f, S);
     if (a.amax_in && a.amax_acc) a.amax_acc[g] = a.amax_in[g];
   }
 }
@@ -338,53 +339,57 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
 //                     are not written.
 //   NV4_COLS_BATCHED  matrix s (rows [s*m, (s+1)*m)) -> output rows s*C + c,
 //                     positions [0, m).
-// One workgroup transposes a tile of 256 positions x 64 columns through LDS:
-//   1. 16-byte coalesced loads of the tile's source rows (8 loads per lane in
-//      flight), zero for padding, into LDS [position][column];
-//   2. lane = column, each wave 4 blocks: read 16 values down the column, block
-//      amax, E4M3 scale, 16 E2M1 codes; codes and scales go to an LDS out-tile;
-//   3. coalesced stores: 16 lanes write the 128 code bytes (and 16 scale bytes)
-//      of one output row of the tile.
-constexpr int kColP = 256;          // positions per tile (16 blocks)
-constexpr int kColC = 64;           // columns per tile
-constexpr int kOutPitch = 136;      // LDS out-tile row pitch (bytes), breaks bank aliasing
-constexpr int kScalePitch = 20;
+// One workgroup transposes a tile of P positions x C columns through LDS:
+//   1. 16-byte coalesced loads of the tile's source rows (all loads of a lane in
+//      flight together), zero for padding, into LDS [position][column];
+//   2. one lane per column: read 16 values down the column, block amax, E4M3
+//      scale, 16 E2M1 codes, into an LDS out-tile;
+//   3. coalesced stores: 8 lanes write one output row's P/2 code bytes.
+// With ROWS_TOO (NV4_ROWS_AND_COLS) the same tile also yields the row-direction
+// quantisation of its rows (blocks of 16 columns), so the source is read once for
+// both operands of a tensor that feeds a data gradient and a weight gradient.
+constexpr int kOutPitch = 72;       // LDS out-tile row pitch for 64 code bytes (+8 breaks bank aliasing)
+constexpr int kScalePitch = 12;
 
-template <bool F32>
+template <bool F32, int P, int C, bool ROWS_TOO>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles_per_seg) {
   typedef typename std::conditional<F32, float, uint16_t>::type T;
-  constexpr int kVec = 16 / sizeof(T);               // elements per 16-byte load
-  constexpr int kLanesPerRow = kColC / kVec;         // 8 (BF16) or 16 (FP32)
+  static_assert(P == 128, "tiles of 128 positions (8 blocks)");
+  constexpr int NB = P / 16;                          // blocks per column per tile
+  constexpr int kVec = 16 / sizeof(T);                // elements per 16-byte load
+  constexpr int kLanesPerRow = C / kVec;
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-  constexpr int kPasses = kColP / kRowsPerPass;      // 8 or 16
-  __shared__ __attribute__((aligned(16))) T tile[kColP][kColC];
-  __shared__ __attribute__((aligned(16))) uint8_t ocodes[kColC][kOutPitch];
-  __shared__ uint8_t oscales[kColC][kScalePitch];
-  __shared__ int64_t bsrc[16];
-  __shared__ int bnum[16], bgrp[16];
+  constexpr int kPasses = P / kRowsPerPass;
+  constexpr int kColGroups = kThreads / C;            // threads per column in phase 2
+  constexpr int kBlkPerThread = NB / kColGroups;
+  __shared__ __attribute__((aligned(16))) T tile[P][C];
+  __shared__ __attribute__((aligned(16))) uint8_t ocodes[C][kOutPitch];
+  __shared__ uint8_t oscales[C][kScalePitch];
+  __shared__ int64_t bsrc[NB];
+  __shared__ int bnum[NB], bgrp[NB];
   __shared__ float inv_tab[128];
 
   if (blockIdx.x == 0 && blockIdx.y == 0) write_group_scales(a);
   const float *A = amax_src(a);
-  const int64_t C = a.K;  // columns of x
-  const int64_t c0 = (int64_t)blockIdx.x * kColC;
+  const int64_t Ccols = a.K;  // columns of x
+  const int64_t c0 = (int64_t)blockIdx.x * C;
   const bool batched = a.layout == NV4_COLS_BATCHED;
   int s_tile = 0;
   int64_t p0, plimit, orow0;
   if (batched) {
     s_tile = blockIdx.y / ptiles_per_seg;
-    p0 = (int64_t)(blockIdx.y % ptiles_per_seg) * kColP;
+    p0 = (int64_t)(blockIdx.y % ptiles_per_seg) * P;
     plimit = a.rows / a.nseg;
-    orow0 = (int64_t)s_tile * C + c0;
+    orow0 = (int64_t)s_tile * Ccols + c0;
   } else {
-    p0 = (int64_t)blockIdx.y * kColP;
+    p0 = (int64_t)blockIdx.y * P;
     plimit = a.seg_padded_offsets[a.nseg];
     orow0 = c0;
   }
   if (p0 >= plimit) return;  // uniform over the workgroup
   const bool seg_scales = a.scale_mode == NV4_SCALE_SEGMENT;
   // per-block source rows: start, count (0..16), scale group
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < NB) {
     const int j = threadIdx.x;
     const int64_t p = p0 + 16 * j;
     int64_t start = 0;
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   // 1. load the tile
   {
     const int lr = threadIdx.x / kLanesPerRow, lc = (threadIdx.x % kLanesPerRow) * kVec;
-    const bool col_ok = c0 + lc < C;
+    const bool col_ok = c0 + lc < Ccols;
     uint4 v[kPasses];
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
@@ -438,51 +443,84 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   }
   __syncthreads();
 
-  // 2. quantise: lane = column, wave w = blocks 4w .. 4w+3
   bool bad = false;
+  auto quant16 = [&](const float v[16], float S, bool use_tab, uint32_t &lo, uint32_t &hi) -> uint32_t {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float av = fabsf(v[i]);
+      bad |= !(av <= 3.402823466e38f);
+      m = fmaxf(m, av);
+    }
+    const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
+    const float inv = use_tab ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
+    lo = 0;
+    hi = 0;
+    lo = pack_e2m1_pair<0>(lo, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
+    lo = pack_e2m1_pair<1>(lo, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
+    lo = pack_e2m1_pair<2>(lo, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
+    lo = pack_e2m1_pair<3>(lo, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
+    hi = pack_e2m1_pair<0>(hi, __fmul_rn(v[8], inv), __fmul_rn(v[9], inv));
+    hi = pack_e2m1_pair<1>(hi, __fmul_rn(v[10], inv), __fmul_rn(v[11], inv));
+    hi = pack_e2m1_pair<2>(hi, __fmul_rn(v[12], inv), __fmul_rn(v[13], inv));
+    hi = pack_e2m1_pair<3>(hi, __fmul_rn(v[14], inv), __fmul_rn(v[15], inv));
+    return sf;
+  };
+  auto tval = [&](int pp, int cc) -> float {
+    const T t = tile[pp][cc];
+    return F32 ? (float)t : __uint_as_float((uint32_t)t << 16);
+  };
+
+  // 2. column blocks: lane = column, kColGroups threads per column share its blocks
   {
-    const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = threadIdx.x % C, grp = threadIdx.x / C;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = w * 4 + jj;
+    for (int jj = 0; jj < kBlkPerThread; ++jj) {
+      const int j = grp * kBlkPerThread + jj;
       float v[16];
-      float m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const T t = tile[16 * j + i][c];
-        v[i] = F32 ? (float)t : __uint_as_float((uint32_t)t << 16);
-        const float av = fabsf(v[i]);
-        bad |= !(av <= 3.402823466e38f);
-        m = fmaxf(m, av);
-      }
-      float S = S_tile;
-      if (!uniform) S = tensor_encode_scale(A[bgrp[j]]);
-      const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
-      const float inv = uniform ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
-      uint32_t lo = 0, hi = 0;
-      lo = pack_e2m1_pair<0>(lo, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
-      lo = pack_e2m1_pair<1>(lo, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
-      lo = pack_e2m1_pair<2>(lo, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
-      lo = pack_e2m1_pair<3>(lo, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
-      hi = pack_e2m1_pair<0>(hi, __fmul_rn(v[8], inv), __fmul_rn(v[9], inv));
-      hi = pack_e2m1_pair<1>(hi, __fmul_rn(v[10], inv), __fmul_rn(v[11], inv));
-      hi = pack_e2m1_pair<2>(hi, __fmul_rn(v[12], inv), __fmul_rn(v[13], inv));
-      hi = pack_e2m1_pair<3>(hi, __fmul_rn(v[14], inv), __fmul_rn(v[15], inv));
+      for (int i = 0; i < 16; ++i) v[i] = tval(16 * j + i, c);
+      const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[j]]);
+      uint32_t lo, hi;
+      const uint32_t sf = quant16(v, S, uniform, lo, hi);
       *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(lo, hi);
       oscales[c][j] = (uint8_t)sf;
     }
   }
+  // 2b. row blocks of the tile's valid rows (tensor scale): each thread one row and
+  // a run of 4 blocks of 16 columns (32 code bytes, 4 scale bytes)
+  if (ROWS_TOO) {
+    constexpr int kRunsPerRow = C / 64;
+    const int pp = threadIdx.x / kRunsPerRow, run = threadIdx.x % kRunsPerRow;
+    const int j = pp >> 4, r = pp & 15;
+    if (pp < P && r < bnum[j] && c0 + run * 64 < Ccols) {
+      const int64_t orow = bsrc[j] + r;  // logical row of x
+      uint32_t cw[8], sfw = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = tval(pp, run * 64 + b * 16 + i);
+        const uint32_t sf = quant16(v, S_tile, true, cw[2 * b], cw[2 * b + 1]);
+        sfw |= sf << (8 * b);
+      }
+      uint8_t *dst = a.codes2 + orow * (Ccols >> 1) + ((c0 + run * 64) >> 1);
+      *reinterpret_cast<uint4 *>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+      *reinterpret_cast<uint32_t *>(a.scales2 + orow * (Ccols >> 4) + ((c0 + run * 64) >> 4)) = sfw;
+    }
+  }
   __syncthreads();
 
-  // 3. coalesced stores: 16 lanes per output row, one block (8 code bytes) each
+  // 3. coalesced stores: 8 lanes per output row, one block (8 code bytes) each
   {
-    const int j = threadIdx.x & 15, rr = threadIdx.x >> 4;
+    const int j = threadIdx.x & 7, rr = threadIdx.x >> 3;
     const bool blk_ok = p0 + 16 * j < plimit;
     const int64_t cstride = a.out_K >> 1, sstride = a.out_K >> 4;
 #pragma unroll
-    for (int pass = 0; pass < kColC / 16; ++pass) {
-      const int c = pass * 16 + rr;
-      if (blk_ok && c0 + c < C) {
+    for (int pass = 0; pass < C / 32; ++pass) {
+      const int c = pass * 32 + rr;
+      if (blk_ok && c0 + c < Ccols) {
         const int64_t orow = orow0 + c;
         *reinterpret_cast<uint2 *>(a.codes + orow * cstride + (p0 >> 1) + 8 * j) =
             *reinterpret_cast<const uint2 *>(&ocodes[c][8 * j]);
@@ -530,20 +568,30 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
       }
     }
   } else {
-    // tiles of 256 positions x 64 columns; NV4_COLS: an upper bound of the padded
-    // positions (rows + 15 per segment), tiles past the actual end exit at once
-    const unsigned gx = (unsigned)std::max<int64_t>(1, (a.K + kColC - 1) / kColC);
+    // tiles of 128 positions x 128 (BF16) or 64 (FP32) columns; NV4_COLS: an upper
+    // bound of the padded positions (rows + 15 per segment), tiles past the actual
+    // end exit at once
+    constexpr int P = 128;
+    const int C = f32 ? 64 : 128;
+    const unsigned gx = (unsigned)std::max<int64_t>(1, (a.K + C - 1) / C);
     int ptiles;
     unsigned gy;
     if (a.layout == NV4_COLS_BATCHED) {
-      ptiles = (int)((a.rows / a.nseg + kColP - 1) / kColP);
+      ptiles = (int)((a.rows / a.nseg + P - 1) / P);
       gy = (unsigned)(ptiles * a.nseg);
     } else {
       ptiles = 0;
-      gy = (unsigned)std::max<int64_t>(1, (a.rows + 15 * (int64_t)a.nseg + kColP - 1) / kColP);
+      gy = (unsigned)std::max<int64_t>(1, (a.rows + 15 * (int64_t)a.nseg + P - 1) / P);
     }
-    if (f32) k_quant_cols<true><<<dim3(gx, gy), kThreads, 0, stream>>>(a, ptiles);
-    else k_quant_cols<false><<<dim3(gx, gy), kThreads, 0, stream>>>(a, ptiles);
+    const bool both = a.layout == NV4_ROWS_AND_COLS;
+    dim3 grid(gx, gy);
+    if (f32) {
+      if (both) k_quant_cols<true, P, 64, true><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      else k_quant_cols<true, P, 64, false><<<grid, kThreads, 0, stream>>>(a, ptiles);
+    } else {
+      if (both) k_quant_cols<false, P, 128, true><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      else k_quant_cols<false, P, 128, false><<<grid, kThreads, 0, stream>>>(a, ptiles);
+    }
   }
   return hipGetLastError();
 }

@@ -53,7 +53,7 @@ def _q(lib, **kw):
     return lib.nvfp4_quantize(ctypes.c_void_p(kw.get("x", 0x1000)), kw.get("xt", 0), kw.get("rows", 32),
                               kw.get("K", 64), kw.get("ldx", 64), kw.get("row_index"), kw.get("layout", 1),
                               kw.get("mode", 0),
-                              kw.get("nseg", 1), None, None, None, None, ctypes.byref(d),
+                              kw.get("nseg", 1), None, None, None, None, ctypes.byref(d), kw.get("out_rows"),
                               ctypes.c_void_p(0x1000), 1 << 20, None, None)
 
 
@@ -74,7 +74,10 @@ def test_quantize_validation(lib):
     assert _q(lib, layout=3, nseg=2, orows=2 * 64, oK=16, row_index=ctypes.c_void_p(0x1000)) == -3
     d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 32, 64, 0, 1)
     assert lib.nvfp4_quantize(ctypes.c_void_p(0x1000), 0, 32, 64, 64, None, 1, 0, 1, None, None, None, None,
-                              ctypes.byref(d), None, 0, None, None) == -4      # no workspace
+                              ctypes.byref(d), None, None, 0, None, None) == -4      # no workspace
+    # rows-and-columns: tensor scale only, needs out_rows of the source shape
+    assert _q(lib, layout=4, mode=1, nseg=2, orows=64, oK=128) == -3
+    assert _q(lib, layout=4, orows=64, oK=128) == -1          # no out_rows
 
 
 def test_permute_validation(lib):

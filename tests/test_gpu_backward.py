@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-def _layer(gpu_lib, cfg, dgrad_dtype=torch.float32):
+def _layer(gpu_lib, cfg, dgrad_dtype=torch.float32, dual=True):
     d = synth.layer_inputs(cfg, with_grads=True)
     W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
     w = gpu_lib.quantize_expert_weights(W13, W2)
@@ -26,7 +26,7 @@ def _layer(gpu_lib, cfg, dgrad_dtype=torch.float32):
     f = gpu_lib.moe_forward(x, lg, w, cfg.k)
     dY2, dY13 = dev_bf16(d["dY2"]), dev_bf16(d["dY13"])
     bufs = gpu_lib.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, dgrad_dtype=dgrad_dtype)
-    b = gpu_lib.moe_backward(x, f, wt, dY2, dY13, bufs)
+    b = gpu_lib.moe_backward(x, f, wt, dY2, dY13, bufs, dual=dual)
     torch.cuda.synchronize()
     return d, (x, dY2, dY13), f, wt, b
 
@@ -44,10 +44,11 @@ def _exact_cols(t, ref):
     assert host(t.tscale)[0] == ref.G[0]
 
 
-def test_tiny_backward_stagewise(gpu_lib):
+@pytest.mark.parametrize("dual", [True, False])
+def test_tiny_backward_stagewise(gpu_lib, dual):
     cfg = synth.CONFIGS["tiny"]
     E, H, I = cfg.E, cfg.H, cfg.I
-    d, _, f, wt, b = _layer(gpu_lib, cfg)
+    d, _, f, wt, b = _layer(gpu_lib, cfg, dual=dual)
     rt = f.routing
     off = host(rt.offsets)
     # S8: upstream gradients quantised along their rows (the dgrad contraction)

@@ -138,3 +138,47 @@ def test_columns_batched_weights(gpu_lib):
     t = gpu_lib.nvfp4_quantize(dev_bf16(x), layout=gpu_lib.NV4_COLS_BATCHED, scale_mode=gpu_lib.NV4_SCALE_SEGMENT,
                                nseg=cfg.E)
     _assert_exact(t, Q.quantize_cols_batched(x, cfg.E))
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_rows_and_columns_in_one_pass(gpu_lib, xdtype):
+    """NV4_ROWS_AND_COLS: the column (token-direction, per segment) and the row
+    quantisation of one tensor from a single read, one tensor scale: both equal the
+    oracle's separate quantisations bit for bit (ragged segments, an empty one,
+    columns not a multiple of the tile width)."""
+    cfg = synth.CONFIGS["tiny"]
+    C = 192
+    x = synth.activations(cfg.R, C, 21)
+    counts = np.bincount(synth.rng(22).integers(0, cfg.E, cfg.R), minlength=cfg.E)
+    counts[5] = 0
+    counts[0] += cfg.R - counts.sum()
+    off = np.concatenate([[0], np.cumsum(counts)])
+    po = Q.padded_offsets(off)
+    xd = dev_bf16(x) if xdtype == "bf16" else dev_f32(x)
+    t = gpu_lib.nvfp4_quantize(xd, layout=gpu_lib.NV4_ROWS_AND_COLS, nseg=cfg.E, seg_offsets=dev_i32(off),
+                               seg_padded_offsets=dev_i32(po))
+    ref_c, _ = Q.quantize_cols(x, off)
+    Kp = int(po[-1])
+    assert np.array_equal(host(t.codes)[:, : Kp // 2], ref_c.packed())
+    assert np.array_equal(host(t.scales)[:, : Kp // 16], ref_c.scales)
+    assert host(t.tscale)[0] == ref_c.G[0]
+    _assert_exact(t.rows_out, Q.quantize_rows(x))
+
+
+def test_rows_and_columns_with_row_gather(gpu_lib):
+    """The fused gather (row_index) with the rows-and-columns layout: the row output
+    is the quantisation of the gathered rows, the column output that of their
+    transpose per segment."""
+    T, C, R = 300, 128, 900
+    x = synth.activations(T, C, 23)
+    idx = synth.rng(24).integers(0, T, R).astype(np.int32)
+    idx[:T] = np.arange(T)  # every row appears, so the gathered amax is the tensor's
+    off = np.array([0, 400, 400, 900])
+    po = Q.padded_offsets(off)
+    t = gpu_lib.nvfp4_quantize(dev_bf16(x), layout=gpu_lib.NV4_ROWS_AND_COLS, nseg=3, seg_offsets=dev_i32(off),
+                               seg_padded_offsets=dev_i32(po), row_index=dev_i32(idx))
+    xg = x[idx]
+    ref_c, _ = Q.quantize_cols(xg, off)
+    Kp = int(po[-1])
+    assert np.array_equal(host(t.codes)[:, : Kp // 2], ref_c.packed())
+    _assert_exact(t.rows_out, Q.quantize_rows(xg))
