@@ -92,11 +92,49 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Buffer stores of one C row: `base` is the row's first byte and `bytes` the part of
+// the tile's rows that lies at or after it, so a store whose byte offset falls
+// outside [0, bytes) is dropped by the hardware (rows past the tile's valid rows,
+// columns flagged invalid by an offset of 2^31).  Device-only helpers: the buffer
+// resource type exists only on the GPU target.
+// (base and bytes are the same for the whole wave; reading them from the first
+// lane keeps the buffer descriptor in scalar registers)
+__device__ __forceinline__ void *uniform_ptr(void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void store_row_b32(void *base, uint32_t bytes, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(
+      __builtin_bit_cast(uint32_t, v),
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                        0x00020000),
+      voff, 0, 0);
+}
+__device__ __forceinline__ void store_row_b16(void *base, uint32_t bytes, uint32_t voff, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(
+      v,
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                        0x00020000),
+      voff, 0, 0);
+}
+// FP32 -> BF16 bits, round to nearest even (the gfx950 converter)
+__device__ __forceinline__ uint16_t bf16_of(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
 // LDS position of 16-byte chunk q (0..3) of tile row r (rows are 64 bytes).  A
 // fragment read has 16 consecutive rows read the same chunk in one LDS pass
 // (64 banks of 4 bytes); XOR-ing the chunk with bits 2..3 of the row gives those
 // 16 rows 16 distinct (row mod 4, position) bank groups.
 __device__ __forceinline__ int swz(int q, int r) { return q ^ ((r >> 2) & 3); }
+
+// A value the whole wave agrees on, as a scalar (lets the compiler keep it, and
+// everything derived from it, in scalar registers)
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 struct TileJob {
   int e;
@@ -193,7 +231,8 @@ void k_gemm(GemmArgs g) {
   __shared__ int tstart[kMaxExperts + 1];
   __shared__ int scratch[NT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave (scalar)
   const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
   const int h = lane >> 5, l32 = lane & 31;
   const int E = g.E;
@@ -258,6 +297,14 @@ void k_gemm(GemmArgs g) {
       job.k_lo = g.offsets[job.e];
       job.k_hi = g.offsets[job.e + 1];
     }
+    // the tile is the same for the whole wave (the expert search read LDS)
+    job.e = __builtin_amdgcn_readfirstlane(job.e);
+    job.m0 = uniform64(job.m0);
+    job.m_end = uniform64(job.m_end);
+    job.n0 = uniform64(job.n0);
+    job.k_lo = uniform64(job.k_lo);
+    job.k_hi = uniform64(job.k_hi);
+    nt_idx = uniform64(nt_idx);
 
     // ---- this lane's DMA sources: byte offsets into the operand; rows outside the
     // tile's range point past the end of the operand, so they load as zeros.
@@ -415,67 +462,85 @@ void k_gemm(GemmArgs g) {
     // every LDS read of this tile has been consumed; the next tile refills the ring
     block_barrier();
 
-    // ---- epilogue: tensor scales, optional SwiGLU, store (32-bit element offsets;
-    // the caller's C is below 2^31 elements)
+    // ---- epilogue: tensor scales, optional SwiGLU, store
     float b_ts = 1.0f;
     if (GROUP == NV4_GROUP_M) b_ts = g.b_scale_mode == NV4_SCALE_SEGMENT ? g.b_tscale[job.e] : g.b_tscale[0];
     else b_ts = g.b_tscale[0];
     const int ldc = (int)g.ldc;
-    const int row0 = (int)job.m0 + wm * FM * 32 + h * 4;
-    const int rows_left = (int)(job.m_end - job.m0) - wm * FM * 32 - h * 4;  // rows r with r < rows_left are valid
-    int col0, ncols;
+    int colw, ncols;  // first output column of this wave's fragment 0 (before the lane), column count
     if (EPI == NV4_EPI_SWIGLU) {
-      col0 = (int)nt_idx * (BN / 2) + wn * (FN / 2 * 32) + l32;
+      colw = (int)nt_idx * (BN / 2) + wn * (FN / 2 * 32);
       ncols = (int)g.N;
     } else if (GROUP == NV4_GROUP_M) {
-      col0 = (int)nt_idx * BN + wn * FN * 32 + l32;
+      colw = (int)nt_idx * BN + wn * FN * 32;
       ncols = (int)g.N;
     } else {
-      col0 = (int)job.n0 + wn * FN * 32 + l32;
+      colw = (int)job.n0 + wn * FN * 32;
       ncols = (int)g.b_rows;
     }
-    const int cbase = GROUP == NV4_GROUP_K ? job.e * (int)g.a_rows * ldc : 0;
+    constexpr int ESZ = OUT_F32 ? 4 : 2;
+    constexpr int NJ = EPI == NV4_EPI_SWIGLU ? FN / 2 : FN;
+    const int rows_valid = (int)std::min<int64_t>(job.m_end - job.m0, BM) - wm * FM * 32;
+    // this wave's rows start at tile row wm*FM*32; lane half h adds 4 rows
+    char *cw = static_cast<char *>(g.C) +
+               ((int64_t)(GROUP == NV4_GROUP_K ? job.e * g.a_rows : 0) + job.m0 + wm * FM * 32) * g.ldc * ESZ;
+    // lane offsets: row q (0..3) of a 4-row group plus 4 rows for lane half h, column
+    // of fragment j (an invalid column gets an offset past any buffer)
+    uint32_t voff[4][NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = colw + j * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        voff[q][j] = col < ncols ? (uint32_t)(((q + h * 4) * ldc + col) * ESZ) : 0x80000000u;
+    }
+    const float sc = a_ts * b_ts;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = i * 32 + (r >> 2) * 8 + (r & 3);
-        if (rl >= rows_left) continue;
-        const int grow = row0 + rl;
-        float sc = a_ts * b_ts;
-        if (A_ROW_SCALE) {
-          const int64_t pr = job.gather ? min_row(g.a_rows_index[grow], g.a_rows) : grow;
-          sc = g.a_tscale[pr] * b_ts;
-        }
-        const int rbase = cbase + grow * ldc;
-        if (EPI == NV4_EPI_SWIGLU) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ru = i * 32 + g4 * 8;  // first row of the group for lane half 0
+        // bytes from row ru to the end of the valid rows, at most 8 rows (the group's
+        // offsets stay below 8 rows)
+        const int left = std::min(std::max(rows_valid - ru, 0), 8);
+        char *rb = cw + (int64_t)ru * g.ldc * ESZ;
+        const uint32_t nb = (uint32_t)(left * ldc * ESZ);
 #pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const int col = col0 + j * 32;
-            if (col >= ncols) continue;
-            const float gt = acc[i][j][r] * sc;
-            const float up = acc[i][j + FN / 2][r] * sc;
-            // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
-            const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-            float stored;
-            if (OUT_F32) {
-              reinterpret_cast<float *>(g.C)[rbase + col] = hv;
-              stored = hv;
-            } else {
-              const uint32_t b16 = f32_to_bf16_rne(hv);
-              reinterpret_cast<uint16_t *>(g.C)[rbase + col] = (uint16_t)b16;
-              stored = bf16_bits_to_f32(b16);
-            }
-            amax_run = fmaxf(amax_run, fabsf(stored));
+        for (int q = 0; q < 4; ++q) {
+          const int r = g4 * 4 + q;
+          float rsc = sc;
+          if (A_ROW_SCALE) {
+            const int rl = ru + q + h * 4;
+            const int64_t grow = job.m0 + wm * FM * 32 + std::min(rl, std::max(rows_valid - 1, 0));
+            const int64_t pr = job.gather ? min_row(g.a_rows_index[grow], g.a_rows) : grow;
+            rsc = g.a_tscale[pr] * b_ts;
           }
-        } else {
+          if (EPI == NV4_EPI_SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = col0 + j * 32;
-            if (col >= ncols) continue;
-            const float v = acc[i][j][r] * sc;
-            if (OUT_F32) reinterpret_cast<float *>(g.C)[rbase + col] = v;
-            else reinterpret_cast<uint16_t *>(g.C)[rbase + col] = (uint16_t)f32_to_bf16_rne(v);
+            for (int j = 0; j < NJ; ++j) {
+              const float gt = acc[i][j][r] * rsc;
+              const float up = acc[i][j + FN / 2][r] * rsc;
+              // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
+              const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+              float stored;
+              if (OUT_F32) {
+                store_row_b32(rb, nb, voff[q][j], hv);
+                stored = hv;
+              } else {
+                const uint16_t b16 = bf16_of(hv);
+                store_row_b16(rb, nb, voff[q][j], b16);
+                stored = bf16_bits_to_f32(b16);
+              }
+              // rows and columns outside the tile hold exact zeros (zero operands)
+              amax_run = fmaxf(amax_run, fabsf(stored));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const float v = acc[i][j][r] * rsc;
+              if (OUT_F32) store_row_b32(rb, nb, voff[q][j], v);
+              else store_row_b16(rb, nb, voff[q][j], bf16_of(v));
+            }
           }
         }
       }
