@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="learner_64k")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--token-scale", action="store_true",
+                    help="per-token FP32 scales for X and the SwiGLU output instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (three times): the known-size kernel whose "
@@ -230,7 +232,7 @@ def main():
         torch.cuda.synchronize()
         wq_ms.append(e0.elapsed_time(e1))
 
-    fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, token_scale=args.token_scale)
     bb = nv4.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I) if backward else None
 
     def step(ev=None):
@@ -296,7 +298,8 @@ def main():
         "data": "synthetic (seeded; random-init expert weights N(0,0.02), activations N(0,1) with 0.1% x20 outliers, "
                 "upstream gradients N(0,1e-3))",
         "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE expert layer "
-                               f"{'forward + backward' if backward else 'forward'}",
+                               f"{'forward + backward' if backward else 'forward'}"
+                               f"{', per-token activation scales' if args.token_scale else ''}",
                    "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "intermediate": cfg.I,
                    "routing": cfg.routing, "expert_load_max": int(counts.max()),
                    "expert_load_min": int(counts.min()), "empty_experts": int((counts == 0).sum()),

@@ -302,18 +302,25 @@ class ForwardBuffers:
     pws: torch.Tensor
     hq_ws: torch.Tensor
     routing: Routing | None = None
+    token_scale: bool = False   # per-token FP32 scales for X and the SwiGLU output
+    hamax_rows: torch.Tensor | None = None  # per-row amax of the SwiGLU output (per-token mode)
 
 
 def alloc_forward(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat16, hact_dtype=torch.bfloat16,
-                  device="cuda") -> ForwardBuffers:
+                  device="cuda", token_scale: bool = False) -> ForwardBuffers:
+    """token_scale: X and the SwiGLU output carry one FP32 scale per row (the
+    per-token recipe) instead of one per tensor."""
     lib = load()
     R = T * k
     return ForwardBuffers(
-        xq=NVFP4.empty(T, H, 1, device), xamax=torch.zeros((1,), dtype=torch.float32, device=device),
+        xq=NVFP4.empty(T, H, T if token_scale else 1, device),
+        xamax=torch.zeros((T if token_scale else 1,), dtype=torch.float32, device=device),
         xg=NVFP4.empty(R, H, 1, device),
         hact=torch.empty((R, I), dtype=hact_dtype, device=device),
         hamax=torch.zeros((1,), dtype=torch.float32, device=device),
-        hq=NVFP4.empty(R, I, 1, device),
+        hq=NVFP4.empty(R, I, R if token_scale else 1, device),
+        token_scale=token_scale,
+        hamax_rows=torch.zeros((R,), dtype=torch.float32, device=device) if token_scale else None,
         y=torch.empty((R, H), dtype=torch.float32, device=device),
         out=torch.empty((T, H), dtype=out_dtype, device=device),
         pws=torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device),
@@ -346,9 +353,12 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
     if bufs is None:
         bufs = alloc_forward(T, H, w.E, k, w.I, device=x.device)
     R = T * k
+    mode = NV4_SCALE_ROW if bufs.token_scale else NV4_SCALE_TENSOR
+    if bufs.token_scale and not fuse_gather:
+        raise ValueError("per-token scales are used with the fused gather")
     st = stream if stream is not None else torch.cuda.current_stream()
     with _Stage(stage_events, "quantize_x", st):
-        nvfp4_quantize(x, out=bufs.xq, amax_out=bufs.xamax, stream=stream)
+        nvfp4_quantize(x, scale_mode=mode, out=bufs.xq, amax_out=bufs.xamax, stream=stream)
     with _Stage(stage_events, "route_permute", st):
         if fuse_gather:
             bufs.routing = moe_permute(logits, w.E, k, ws=bufs.pws, stream=stream, out=bufs.routing)
@@ -363,7 +373,10 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
         nvfp4_grouped_gemm(a, w.w13, bufs.routing.offsets, w.E, w.I, M_cap=R, a_rows=a_rows,
                            epilogue=NV4_EPI_SWIGLU, C=bufs.hact, amax_out=bufs.hamax, stream=stream)
     with _Stage(stage_events, "quantize_hact", st):
-        nvfp4_quantize(bufs.hact, amax_in=bufs.hamax, out=bufs.hq, stream=stream)
+        if bufs.token_scale:
+            nvfp4_quantize(bufs.hact, scale_mode=NV4_SCALE_ROW, out=bufs.hq, amax_out=bufs.hamax_rows, stream=stream)
+        else:
+            nvfp4_quantize(bufs.hact, amax_in=bufs.hamax, out=bufs.hq, stream=stream)
     with _Stage(stage_events, "gemm2", st):
         nvfp4_grouped_gemm(bufs.hq, w.w2, bufs.routing.offsets, w.E, H, M_cap=R, C=bufs.y, stream=stream)
     with _Stage(stage_events, "combine", st):
@@ -413,6 +426,8 @@ class BackwardBuffers:
     xc: NVFP4               # [H, Kcap]
     dw2: torch.Tensor       # [E, H, I]
     dw13: torch.Tensor      # [E, 2I, H]
+    x_amax: torch.Tensor | None = None  # tensor amax of X when the forward scaled per token
+    x_tq: NVFP4 | None = None            # (its by-product: X quantised with one tensor scale)
 
 
 def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfloat16, wgrad_dtype=torch.float32,
@@ -427,7 +442,8 @@ def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfl
         dy2c=NVFP4.empty(H, kc, 1, device), hc=NVFP4.empty(I, kc, 1, device),
         dy13c=NVFP4.empty(2 * I, kc, 1, device), xc=NVFP4.empty(H, kc, 1, device),
         dw2=torch.empty((E, H, I), dtype=wgrad_dtype, device=device),
-        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device))
+        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device),
+        x_amax=torch.zeros((1,), dtype=torch.float32, device=device))
 
 
 def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY2: torch.Tensor,
@@ -485,7 +501,16 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
         with _Stage(stage_events, "quantize_cols_dy13", st):
             nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
     with _Stage(stage_events, "quantize_cols_x", st):
-        nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
+        if fwd.token_scale:
+            # the forward kept per-token amaxes: the tensor's comes from one quantisation
+            # pass over X itself (T rows) rather than an amax pass over the k-times
+            # gathered rows
+            if bufs.x_tq is None or bufs.x_tq.rows != T:
+                bufs.x_tq = NVFP4.empty(T, H, 1, device=x.device)
+            nvfp4_quantize(x, out=bufs.x_tq, amax_out=bufs.x_amax, stream=stream)
+            nvfp4_quantize(x, amax_in=bufs.x_amax, out=bufs.xc, row_index=rt.row_token, **seg)
+        else:
+            nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
     with _Stage(stage_events, "wgrad_w13", st):
         nvfp4_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
                            stream=stream)

@@ -230,6 +230,9 @@ void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? Cfg::kStageBytes : 16];
   __shared__ int tstart[kMaxExperts + 1];
   __shared__ int scratch[NT];
+  // per-row A scales of the tile (per-token mode), double-buffered by tile parity: a
+  // wave writes the next tile's scales while others may still read this tile's
+  __shared__ float row_scale[A_ROW_SCALE ? 2 : 1][A_ROW_SCALE ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave (scalar)
@@ -305,6 +308,17 @@ void k_gemm(GemmArgs g) {
     job.k_lo = uniform64(job.k_lo);
     job.k_hi = uniform64(job.k_hi);
     nt_idx = uniform64(nt_idx);
+
+    if (A_ROW_SCALE) {
+      // the tile's row scales, fetched now so that the epilogue reads them from LDS
+      // (every wave's writes are complete by the barrier that ends the K loop)
+      for (int t = tid; t < BM; t += NT) {
+        const int64_t grow = job.m0 + t;
+        float v = 0.0f;
+        if (grow < job.m_end) v = g.a_tscale[job.gather ? min_row(g.a_rows_index[grow], g.a_rows) : grow];
+        row_scale[it & 1][t] = v;
+      }
+    }
 
     // ---- this lane's DMA sources: byte offsets into the operand; rows outside the
     // tile's range point past the end of the operand, so they load as zeros.
@@ -460,6 +474,7 @@ void k_gemm(GemmArgs g) {
       }
     }
     // every LDS read of this tile has been consumed; the next tile refills the ring
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     block_barrier();
 
     // ---- epilogue: tensor scales, optional SwiGLU, store
@@ -509,12 +524,7 @@ void k_gemm(GemmArgs g) {
         for (int q = 0; q < 4; ++q) {
           const int r = g4 * 4 + q;
           float rsc = sc;
-          if (A_ROW_SCALE) {
-            const int rl = ru + q + h * 4;
-            const int64_t grow = job.m0 + wm * FM * 32 + std::min(rl, std::max(rows_valid - 1, 0));
-            const int64_t pr = job.gather ? min_row(g.a_rows_index[grow], g.a_rows) : grow;
-            rsc = g.a_tscale[pr] * b_ts;
-          }
+          if (A_ROW_SCALE) rsc = row_scale[it & 1][wm * FM * 32 + ru + q + h * 4] * b_ts;
           if (EPI == NV4_EPI_SWIGLU) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {

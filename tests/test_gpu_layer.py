@@ -87,3 +87,36 @@ def test_single_expert_top1_is_dense_mlp(gpu_lib):
     assert np.array_equal(host(b.routing.row_token), np.arange(T))
     y_ref = moe.grouped_gemm_m(nvfp4_host(b.hq).dequant(), nvfp4_host(w.w2).dequant(), [0, T], 1, H)
     assert rel_frob(host(b.y), y_ref) <= TOL
+
+
+def test_tiny_forward_per_token_scales(gpu_lib):
+    """The per-token recipe (one FP32 scale per row of X and of the SwiGLU output):
+    codes and scales bit-exact, GEMMs within 1e-5 of the oracle on the GPU's
+    operands, and the backward still runs (tensor amax of X taken there)."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    x, lg = dev_bf16(d["X"]), dev_f32(d["logits"])
+    bufs = gpu_lib.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, out_dtype=torch.float32, token_scale=True)
+    b = gpu_lib.moe_forward(x, lg, w, cfg.k, bufs)
+    torch.cuda.synchronize()
+    rt = b.routing
+    xq_ref = Q.quantize_rows(d["X"], "row")
+    assert np.array_equal(host(b.xq.codes), xq_ref.packed()) and np.array_equal(host(b.xq.scales), xq_ref.scales)
+    assert np.array_equal(host(b.xq.tscale), xq_ref.G)
+    A = nvfp4_host(b.xq).dequant()[host(rt.row_token)]
+    h_ref = moe.swiglu(moe.grouped_gemm_m(A, nvfp4_host(w.w13).dequant(), host(rt.offsets), cfg.E, 2 * cfg.I))
+    h = host(b.hact)
+    assert rel_frob(h, bf16_rne_of(h_ref)) <= 1e-2   # BF16 storage of the FP32 SwiGLU output
+    hq_ref = Q.quantize_rows(h, "row")
+    assert np.array_equal(host(b.hq.codes), hq_ref.packed()) and np.array_equal(host(b.hq.tscale), hq_ref.G)
+    y_ref = moe.grouped_gemm_m(nvfp4_host(b.hq).dequant(), nvfp4_host(w.w2).dequant(), host(rt.offsets), cfg.E, cfg.H)
+    assert rel_frob(host(b.y), y_ref) <= TOL
+    assert rel_frob(host(b.out), moe.combine(host(b.y), host(rt.token_row), host(rt.topk_w))) <= TOL
+    wt = gpu_lib.quantize_expert_weights_t(W13, W2)
+    g = gpu_lib.moe_backward(x, b, wt, dev_bf16(d["dY2"]), dev_bf16(d["dY13"]))
+    torch.cuda.synchronize()
+    xc_ref, _ = Q.quantize_cols(d["X"][host(rt.row_token)], host(rt.offsets))
+    Kp = xc_ref.codes.shape[1]
+    assert np.array_equal(host(g.xc.codes)[:, : Kp // 2], xc_ref.packed())
