@@ -182,6 +182,8 @@ def main():
     ap.add_argument("--token-scale", action="store_true",
                     help="per-token FP32 scales for X and the SwiGLU output instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every kernel from Python each step instead of replaying a captured HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (three times): the known-size kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the GEMM's traffic counters")
@@ -245,10 +247,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # the step's ~30 launches captured once into a HIP graph (the library allocates
+    # nothing and clears buffers with kernels, so the step is capturable); each
+    # timed step replays it
+    run = step
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+
     # timed: exactly K steps, synchronised on both sides (wall clock)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -305,6 +324,7 @@ def main():
                    "expert_load_min": int(counts.min()), "empty_experts": int((counts == 0).sum()),
                    "top4_share": round(float(np.sort(counts)[-4:].sum() / counts.sum()), 4),
                    "flops_per_step": flops},
+        "launch": "eager" if args.no_graph else "hip_graph",
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
         "weight_quantize_ms": round(float(np.median(wq_ms)), 4),
         "roofline": {"bound": "mfma", "kernel": gemm[dom][1], "stage": dom,

@@ -120,3 +120,43 @@ def test_tiny_forward_per_token_scales(gpu_lib):
     xc_ref, _ = Q.quantize_cols(d["X"][host(rt.row_token)], host(rt.offsets))
     Kp = xc_ref.codes.shape[1]
     assert np.array_equal(host(g.xc.codes)[:, : Kp // 2], xc_ref.packed())
+
+
+def test_captured_graph_replays_match_eager(gpu_lib):
+    """The whole forward + backward captured into a HIP graph (as the benchmark
+    times it): every replay, with eager work and synchronisations in between,
+    equals the eager result bit for bit."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    wt = gpu_lib.quantize_expert_weights_t(W13, W2)
+    x, lg = dev_bf16(d["X"]), dev_f32(d["logits"])
+    dY2, dY13 = dev_bf16(d["dY2"]), dev_bf16(d["dY13"])
+    fb = gpu_lib.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    bb = gpu_lib.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+
+    def step():
+        gpu_lib.moe_forward(x, lg, w, cfg.k, fb)
+        gpu_lib.moe_backward(x, fb, wt, dY2, dY13, bb)
+
+    step()
+    torch.cuda.synchronize()
+    outs = lambda: [t.clone() for t in (fb.out, fb.hq.codes, bb.dhact, bb.dxperm, bb.dw2, bb.dw13, bb.xc.codes)]
+    ref = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (fb.out, bb.dw2, bb.dxperm):
+            t.fill_(7)           # eager work between replays that the replay must overwrite
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs()):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
