@@ -14,8 +14,8 @@
 //   1. one wave per chunk of kPermuteChunk assignments ranks each assignment
 //      among equal experts inside the chunk (wave ballots over the id bits,
 //      chunk-local counters in LDS), and writes the chunk's expert histogram;
-//   2. one workgroup turns the histograms into per-(chunk, expert) bases and the
-//      expert offsets (exclusive prefix sums);
+//   2. one wave per expert turns the histograms into per-(chunk, expert) bases,
+//      one workgroup the expert totals into the expert offsets (exclusive prefix sums);
 //   3. every assignment's row is base + local rank; a scatter writes the maps.
 // The result is one exactly defined permutation, identical on every run.
 #include <algorithm>
@@ -28,20 +28,52 @@ namespace nv4 {
 namespace {
 
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / kWave;
 
-// one wave per token: softmax statistics, then k rounds of a wave-wide argmax
+// Wave-wide reductions over 64 lanes without LDS: DPP within rows of 16 lanes (the
+// pairs (i, i^1), (i, i^2), then the half-row and row mirrors), then the gfx950
+// row swaps across 16 and 32 lanes.  Every lane ends with the result.
+template <class F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(s16[0], s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(s32[0], s32[1]);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  }));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  return (int)wave_reduce_u32((uint32_t)v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int)x, (int)y); });
+}
+
+// One wave per token, NPL logits per lane (expert e = lane + 64 * i): softmax
+// statistics, then k rounds of a wave-wide argmax.  Each round: every lane's best
+// untaken candidate (larger logit first, then lower id), the wave's maximum value,
+// and among the lanes holding it the lowest id (a ballot; a second reduction only
+// when several lanes tie).
+template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
+  if (t >= a.T) return;  // uniform over the wave
   const int E = a.E;
   const float *lg = a.logits + t * E;
-  float lv[kMaxPerLane];
+  float lv[NPL];
   float mx = -INFINITY;
   bool nan = false;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
     lv[i] = -INFINITY;
     if (e < E) {
@@ -50,14 +82,14 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
       mx = fmaxf(mx, lv[i]);
     }
   }
-  mx = wave_max(mx);
+  mx = wave_max_dpp(mx);
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) s += expf(lv[i] - mx);
   }
-  s = wave_sum(s);
+  s = wave_sum_dpp(s);
   uint32_t taken = 0;
   int my_id = 0;
   float my_w = 0.0f, wsum = 0.0f;
@@ -65,20 +97,25 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
       const int e = lane + kWave * i;
-      if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (lv[i] == bv && e < bi))) { bv = lv[i]; bi = e; }
+      // ids of one lane increase with i, so the first of equal values has the lowest id
+      if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (bi == 0x7FFFFFFF && lv[i] == bv))) { bv = lv[i]; bi = e; }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    const float vmax = wave_max_dpp(bv);
+    const uint64_t cand = __ballot(bi != 0x7FFFFFFF && bv == vmax);
+    int wid;
+    if (cand == 0) {
+      wid = 0x7FFFFFFF;  // every remaining logit is NaN
+    } else if ((cand & (cand - 1)) == 0) {
+      wid = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(cand));
+    } else {
+      wid = wave_min_dpp(((cand >> lane) & 1) ? bi : 0x7FFFFFFF);
     }
-    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);  // (bi == INT_MAX only if every remaining logit is NaN)
-    const float w = expf(bv - mx) / s;
+    if (wid < E && (wid & 63) == lane) taken |= 1u << (wid >> 6);
+    const float w = expf(vmax - mx) / s;
     wsum += w;
-    if (lane == j) { my_id = bi; my_w = w; }
+    if (lane == j) { my_id = wid; my_w = w; }
   }
   if (a.flags & NV4_RENORM) my_w = my_w / wsum;
   if (lane < a.k) {
@@ -125,10 +162,13 @@ __global__ __launch_bounds__(64) void k_rank(PermuteArgs a, int nbits) {
   if (badid && a.dev_status) atomicOr(a.dev_status, kDsBadExpert);
 }
 
-// one workgroup: chunk histograms -> per-(chunk, expert) bases, expert offsets.
-// Each wave takes experts w, w + 16, ...: its lanes hold consecutive chunk counts
-// of the expert and a wave-wide exclusive scan gives the chunk bases; then one
-// block-wide scan over the expert totals gives the offsets.
+// Chunk histograms -> per-(chunk, expert) bases and expert offsets, in two kernels:
+//   k_scan_chunks: one wave per expert turns its column of chunk counts into an
+//     exclusive prefix over the chunks (in place) and leaves the expert's total in
+//     expert_offsets[e];
+//   k_scan_experts: one workgroup turns the totals into the exclusive offsets (and
+//     the 16-padded ones).
+// A row is then chunk base + expert offset + local rank (k_scatter).
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -138,29 +178,26 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-__global__ __launch_bounds__(1024) void k_scan(PermuteArgs a, int nchunks) {
+__global__ __launch_bounds__(64) void k_scan_chunks(PermuteArgs a, int nchunks) {
+  const int E = a.E, e = blockIdx.x, lane = threadIdx.x;
+  int run = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    int *p = a.chunk_counts + (int64_t)c * E + e;
+    const int v = c < nchunks ? *p : 0;
+    const int incl = wave_incl_scan(v, lane);
+    if (c < nchunks) *p = run + incl - v;
+    run += __shfl(incl, 63, kWave);
+  }
+  if (lane == 0) a.expert_offsets[e] = run;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_experts(PermuteArgs a, int have_counts) {
   __shared__ int sc[kMaxE];
   __shared__ int sp[kMaxE];
-  __shared__ int tot[kMaxE];
   const int E = a.E;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // 1. per expert: exclusive prefix over chunks (in place), total
-  for (int e = wave; e < E; e += 16) {
-    int run = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 64) {
-      const int c = c0 + lane;
-      int *p = a.chunk_counts + (int64_t)c * E + e;
-      const int v = c < nchunks ? *p : 0;
-      const int incl = wave_incl_scan(v, lane);
-      if (c < nchunks) *p = run + incl - v;
-      run += __shfl(incl, 63, kWave);
-    }
-    if (lane == 0) tot[e] = run;
-  }
-  __syncthreads();
-  // 2. exclusive scans over experts (counts and 16-padded counts)
-  const int e = tid;
-  const int run = e < E ? tot[e] : 0;
+  const int e = threadIdx.x;
+  const int run = (e < E && have_counts) ? a.expert_offsets[e] : 0;
   const int prun = ((run + 15) >> 4) << 4;
   sc[e] = run;
   sp[e] = prun;
@@ -180,12 +217,7 @@ __global__ __launch_bounds__(1024) void k_scan(PermuteArgs a, int nchunks) {
       a.expert_offsets[E] = sc[e];
       if (a.padded_offsets) a.padded_offsets[E] = sp[e];
     }
-    tot[e] = sc[e] - run;  // exclusive offset of expert e
   }
-  __syncthreads();
-  // 3. chunk bases become absolute rows
-  const int64_t n = (int64_t)nchunks * E;
-  for (int64_t i = tid; i < n; i += 1024) a.chunk_counts[i] += tot[i % E];
 }
 
 __global__ __launch_bounds__(256) void k_scatter(PermuteArgs a) {
@@ -195,7 +227,7 @@ __global__ __launch_bounds__(256) void k_scatter(PermuteArgs a) {
   int e = a.topk_ids[f];
   if (e < 0 || e >= a.E) e = 0;
   const int64_t c = f / kPermuteChunk;
-  const int r = a.chunk_counts[c * a.E + e] + a.local_rank[f];
+  const int r = a.chunk_counts[c * a.E + e] + a.expert_offsets[e] + a.local_rank[f];
   a.row_token[r] = (int)(f / a.k);
   a.token_row[f] = r;
 }
@@ -238,16 +270,23 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream) {
   const int64_t R = a.T * a.k;
   if (R == 0) {
     // no assignment: all offsets are zero
-    PermuteArgs z = a;
-    k_scan<<<1, 1024, 0, stream>>>(z, 0);
+    k_scan_experts<<<1, 1024, 0, stream>>>(a, 0);
     return hipGetLastError();
   }
   const int nchunks = (int)((R + kPermuteChunk - 1) / kPermuteChunk);
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
-  if (a.logits) k_topk<<<(unsigned)((a.T + 3) / 4), 256, 0, stream>>>(a);
+  if (a.logits) {
+    const unsigned gt = (unsigned)((a.T + 3) / 4);
+    if (a.E <= 64) k_topk<1><<<gt, 256, 0, stream>>>(a);
+    else if (a.E <= 128) k_topk<2><<<gt, 256, 0, stream>>>(a);
+    else if (a.E <= 256) k_topk<4><<<gt, 256, 0, stream>>>(a);
+    else if (a.E <= 512) k_topk<8><<<gt, 256, 0, stream>>>(a);
+    else k_topk<16><<<gt, 256, 0, stream>>>(a);
+  }
   k_rank<<<nchunks, 64, 0, stream>>>(a, nbits);
-  k_scan<<<1, 1024, 0, stream>>>(a, nchunks);
+  k_scan_chunks<<<a.E, 64, 0, stream>>>(a, nchunks);
+  k_scan_experts<<<1, 1024, 0, stream>>>(a, 1);
   k_scatter<<<(unsigned)((R + 255) / 256), 256, 0, stream>>>(a);
   if (a.gather_K > 0) k_gather<<<(unsigned)((R + 3) / 4), 256, 0, stream>>>(a);
   return hipGetLastError();
