@@ -108,6 +108,30 @@ def grouped_gemm_k(A_hat: np.ndarray, B_hat: np.ndarray, k_offsets, E: int) -> n
     return C
 
 
+def transpose_segments(x: np.ndarray, seg_offsets) -> tuple[np.ndarray, np.ndarray]:
+    """The column layout of a weight-gradient operand: x [R, C] -> [C, Rpad],
+    segment s (rows [off[s], off[s+1])) in columns [po[s], po[s] + n_s) and
+    zeros in the rest of its range padded to a multiple of 16.  Returns the
+    matrix and the padded offsets po."""
+    x = np.asarray(x)
+    off = np.asarray(seg_offsets, dtype=np.int64)
+    n = np.diff(off)
+    po = np.concatenate([[0], np.cumsum((n + 15) // 16 * 16)]).astype(np.int64)
+    out = np.zeros((x.shape[1], int(po[-1])), dtype=x.dtype)
+    for s in range(len(n)):
+        out[:, po[s]:po[s] + n[s]] = x[off[s]:off[s + 1]].T
+    return out, po
+
+
+def transpose_batched(x: np.ndarray, nbatch: int) -> np.ndarray:
+    """x [nbatch*m, C] (nbatch matrices of m rows) -> [nbatch*C, m]: every matrix
+    transposed in place in the stack (the data-gradient form of expert weights)."""
+    x = np.asarray(x)
+    R, C = x.shape
+    m = R // nbatch
+    return x.reshape(nbatch, m, C).transpose(0, 2, 1).reshape(nbatch * C, m)
+
+
 def silu(g: np.ndarray) -> np.ndarray:
     g = np.asarray(g, dtype=np.float64)
     with np.errstate(over="ignore"):

@@ -36,6 +36,13 @@ supports, used identically by the GPU path):
    consecutive rows of one column, restarting at every segment (expert) start;
    segments are zero-padded to a multiple of 16 rows (padding quantises to
    scale 0, code 0).
+7. BF16 dequantisation (the operands of the dequantized backward, *The 4-bitter
+   Lesson*, section "Improving Gradient Stability": the backward takes the BF16
+   value of DQ(Q(.)) of the very tensor the forward used).  The element value
+   e2m1(q) * sf is exact in FP32 (at most 6 significant bits); it is multiplied
+   by G in one correctly rounded FP32 operation and the product is rounded to
+   BF16 (nearest, ties to even).  This is dequantisation in the quantiser's own
+   precision followed by a cast to the BF16 storage format.
 
 Each FP32 step above is one correctly rounded operation (``formats.f32_div`` and
 ``formats.f32_mul``), so the integer results (codes, scale bytes) are exactly
@@ -219,6 +226,17 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = p & 0xF
     out[..., 1::2] = p >> 4
     return out
+
+
+def dequantize_bf16(t: NVFP4) -> np.ndarray:
+    """Reading 7: the BF16 value of every element of t, returned as float32 values
+    (each exactly a BF16 number)."""
+    vals = F.e2m1_decode(t.codes)
+    rows, K = vals.shape
+    sfv = F.e4m3_decode(t.scales).astype(np.float64)
+    exact = (vals.reshape(rows, K // BLOCK, BLOCK) * sfv[:, :, None]).reshape(rows, K)   # e2m1 * sf, exact
+    G = np.repeat(np.asarray(t.G_block, np.float32), BLOCK, axis=1)
+    return F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32_mul(exact.astype(np.float32), G)))
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, G_block: np.ndarray) -> np.ndarray:

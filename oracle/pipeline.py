@@ -15,6 +15,16 @@ new contraction dimension (the fully quantised recipe, case (a) of *The
 4-bitter Lesson*, section "Results"), starting from upstream gradients dY2 (of
 the down projection's output rows) and dY13 (of the gate/up output rows).
 
+The BF16 variants (*The 4-bitter Lesson*, sections "Why is the NVFP4
+pretraining recipe not sufficient for RL?" and "Improving Gradient Stability"):
+``moe_forward_bf16`` is the unquantised layer (the comparison point for the
+W4A4 forward); ``moe_backward_bf16`` computes the same four gradients with BF16
+operands, either the unquantised tensors (the conservative baseline: the
+backward differentiates x . w although the forward used Q(w)) or the BF16
+dequantised values of the exact NVFP4 tensors of the forward ("dequantized
+backward", applied to weights and activations).  The upstream gradients stay
+BF16 in both.
+
 Storage roundings of the GPU path are mirrored (SwiGLU output stored as BF16,
 expert outputs as FP32), so these functions give an end-to-end oracle result.
 Parity unpinned: after an intermediate tensor is re-quantised, an FP32-vs-FP64
@@ -65,6 +75,71 @@ def moe_forward(X: np.ndarray, logits: np.ndarray, W13: np.ndarray, W2: np.ndarr
         out = F.bf16_bits_to_f32(F.f32_to_bf16_bits(out))
     return dict(topk_ids=ids, topk_w=w, perm=perm, Xq=Xq, Xg=Xg, W13q=W13q, W2q=W2q,
                 C1=C1, Hact=Hact, Hact_bf16=Hact_bf16, Hq=Hq, Y=Y32, out=out)
+
+
+def bf16(x: np.ndarray) -> np.ndarray:
+    """Values rounded to BF16 (nearest, ties to even), as float32."""
+    return F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32(x)))
+
+
+def moe_forward_bf16(X: np.ndarray, logits: np.ndarray, W13: np.ndarray, W2: np.ndarray, k: int,
+                     renorm: bool = False) -> dict:
+    """The unquantised layer on BF16 values: same routing, permutation, SwiGLU
+    and combine as ``moe_forward``, with the GEMMs on the BF16 operands."""
+    X = np.asarray(X, np.float32)
+    T, H = X.shape
+    E, I2, _ = W13.shape
+    I = I2 // 2
+    ids, w = moe.route_topk(logits, k, renorm)
+    perm = moe.permute(ids, E)
+    Xperm = X[np.asarray(perm["row_token"], np.int64)]
+    C1 = moe.grouped_gemm_m(Xperm, np.asarray(W13, np.float32).reshape(E * I2, H), perm["offsets"], E, I2)
+    Hact = moe.swiglu(C1)
+    Hact_bf16 = bf16(Hact)
+    Y = moe.grouped_gemm_m(Hact_bf16, np.asarray(W2, np.float32).reshape(E * H, I), perm["offsets"], E, H)
+    Y32 = F.f32(Y)
+    out = F.f32(moe.combine(Y32, perm["token_row"], w))
+    return dict(topk_ids=ids, topk_w=w, perm=perm, C1=C1, Hact=Hact, Hact_bf16=Hact_bf16, Y=Y32, out=out)
+
+
+def backward_operands_bf16(X: np.ndarray, Hact_bf16: np.ndarray, W13: np.ndarray, W2: np.ndarray,
+                           fwd: dict | None = None) -> dict:
+    """The four BF16 operands of the backward that come from the forward: X, Hact,
+    W13 and W2.  With ``fwd`` (the result of ``moe_forward``) they are the BF16
+    dequantised values of the forward's NVFP4 tensors (reading 7 of ``nvfp4``);
+    without it, the BF16 tensors themselves."""
+    E, I2, H = W13.shape
+    I = I2 // 2
+    if fwd is None:
+        return dict(X=np.asarray(X, np.float32), Hact=np.asarray(Hact_bf16, np.float32),
+                    W13=np.asarray(W13, np.float32).reshape(E * I2, H),
+                    W2=np.asarray(W2, np.float32).reshape(E * H, I))
+    return dict(X=Q.dequantize_bf16(fwd["Xq"]), Hact=Q.dequantize_bf16(fwd["Hq"]),
+                W13=Q.dequantize_bf16(fwd["W13q"]), W2=Q.dequantize_bf16(fwd["W2q"]))
+
+
+def moe_backward_bf16(ops: dict, dY2: np.ndarray, dY13: np.ndarray, perm: dict) -> dict:
+    """The four gradients of ``moe_backward`` with BF16 operands ``ops`` (from
+    ``backward_operands_bf16``; X un-permuted, Hact in expert order) and BF16
+    upstream gradients, FP64 accumulation.  The weight gradients contract over
+    each expert's own rows, laid out as the column operands of the GPU path."""
+    E = len(perm["offsets"]) - 1
+    H = ops["X"].shape[1]
+    I = ops["Hact"].shape[1]
+    off = perm["offsets"]
+    Xperm = ops["X"][np.asarray(perm["row_token"], np.int64)]
+    W2t = moe.transpose_batched(ops["W2"], E)      # [E*I, H]
+    W13t = moe.transpose_batched(ops["W13"], E)    # [E*H, 2I]
+    dHact = moe.grouped_gemm_m(dY2, W2t, off, E, I)
+    dXperm = moe.grouped_gemm_m(dY13, W13t, off, E, H)
+    dY2c, po = moe.transpose_segments(np.asarray(dY2, np.float32), off)
+    Hc, _ = moe.transpose_segments(ops["Hact"], off)
+    dY13c, _ = moe.transpose_segments(np.asarray(dY13, np.float32), off)
+    Xc, _ = moe.transpose_segments(Xperm, off)
+    dW2 = moe.grouped_gemm_k(dY2c, Hc, po, E)
+    dW13 = moe.grouped_gemm_k(dY13c, Xc, po, E)
+    return dict(W2t=W2t, W13t=W13t, dHact=dHact, dXperm=dXperm, dY2c=dY2c, Hc=Hc, dY13c=dY13c, Xc=Xc,
+                padded_offsets=po, dW2=dW2, dW13=dW13)
 
 
 def moe_backward(X: np.ndarray, Hact_bf16: np.ndarray, W13: np.ndarray, W2: np.ndarray,
