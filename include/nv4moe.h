@@ -257,6 +257,72 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
                               void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * nv4_to_bf16 -- BF16 operands for the BF16 and dequantized backward.
+ * [4BL] "Improving Gradient Stability": the dequantized backward runs the
+ * backward GEMMs on BF16 operands holding DQ(Q(.)) of the exact NVFP4 tensors
+ * the forward used, for weights and activations; [4BL] "Why is the NVFP4
+ * pretraining recipe not sufficient for RL?": the conservative baseline keeps the
+ * backward in BF16 on the unquantised tensors.
+ *
+ * The source is either x (BF16 [x_rows][ldx], ldx >= K, ldx % 8 == 0, 16-byte
+ * aligned) or q (an NVFP4 tensor [q->rows][K] with its tscale grouping: per
+ * tensor, per equal segment of q->rows/q->nseg rows, or per row); exactly one is
+ * non-NULL.  The BF16 value of an NVFP4 element is
+ *   bf16_rne(fp32(e2m1(q) * sf * G))
+ * where e2m1(q) * sf is exact and the product with G is one FP32 rounding.
+ *   rows, K          logical rows (after the gather) and columns; K % 16 == 0.
+ *   row_index        device int32 [rows] or NULL (NV4_ROWS, NV4_COLS): logical row
+ *                    r is source row row_index[r] (an index outside the source is
+ *                    clamped into it).
+ *   layout           NV4_ROWS: out [rows][K] (out_rows == rows, out_cols == K).
+ *                    NV4_COLS: out [K][out_cols]; logical row r of segment s
+ *                      (rows [seg_offsets[s], seg_offsets[s+1])) lands in column
+ *                      seg_padded_offsets[s] + r - seg_offsets[s]; the rest of each
+ *                      segment's 16-padded range is written as zeros; columns at
+ *                      and after seg_padded_offsets[nseg] are not written.
+ *                      out_cols >= rows + 15 * nseg, % 8.  The column operands of
+ *                      the weight-gradient GEMMs (bf16_grouped_gemm, NV4_GROUP_K).
+ *                    NV4_COLS_BATCHED: the source is nseg equal matrices of
+ *                      m = rows/nseg rows (m % 16 == 0); out [nseg*K][m] holds each
+ *                      transposed.  The transposed expert weights of the data
+ *                      gradients.
+ *   out              device BF16 [out_rows][out_cols], 16-byte aligned.
+ * Errors: EINVAL (both or neither source, bad sizes, output shape mismatch),
+ * EALIGN (K % 16, ldx, misaligned pointers), EUNSUPPORTED (row_index with
+ * NV4_COLS_BATCHED), EHIP.
+ */
+nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_tensor *q, int64_t rows, int64_t K,
+                       const int32_t *row_index, int layout, int nseg, const int32_t *seg_offsets,
+                       const int32_t *seg_padded_offsets, void *out, int64_t out_rows, int64_t out_cols,
+                       void *stream);
+
+/*
+ * bf16_grouped_gemm -- nvfp4_grouped_gemm's grouping, row gather and epilogues on
+ * BF16 operands (FP32 accumulation, no tensor scales).  [4BL] "Improving Gradient
+ * Stability" (the backward GEMMs on BF16 operands), "Why is the NVFP4 pretraining
+ * recipe not sufficient for RL?" (the BF16 baseline); [LBP] "Throughput Gains and
+ * the Conditions That Produce Them" (the BF16 layer as the comparison point).
+ *
+ *   A [a_rows][K], B [b_rows][K]   BF16, row-major with row stride K, 16-byte
+ *                    aligned, each below 4 GiB.
+ *   K                a positive multiple of 32 (the kernel stages 32 elements).
+ * NV4_GROUP_M: b_rows == E*N (EPI_NONE) or E*2N (EPI_SWIGLU: rows [gate_e; up_e]);
+ *   expert e's rows [offsets[e], offsets[e+1]) of A (or A rows a_rows[r], the
+ *   fused gather) times B_e^T into C [M_cap][ldc]; amax_out as in
+ *   nvfp4_grouped_gemm.
+ * NV4_GROUP_K: A [N][Kcap], B [M][Kcap] with Kcap = K; expert e contracts over
+ *   [offsets[e], offsets[e+1]) (16-aligned, e.g. padded offsets, the layout
+ *   nv4_to_bf16 NV4_COLS writes); C [E][N][ldc] gets A_e . B_e^T, an empty range
+ *   zeros.  N is taken from a_rows.
+ * Errors: EINVAL, EALIGN (K not a positive multiple of 32, misaligned operands),
+ * EUNSUPPORTED (SWIGLU or a row index with GROUP_K), EHIP.
+ */
+nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int64_t b_rows_n, int64_t K,
+                             const int32_t *offsets, int E, int64_t M_cap, int64_t N, const int32_t *a_rows,
+                             int group_mode, int epilogue, void *C, nv4_dtype ctype, int64_t ldc,
+                             float *amax_out, void *stream);
+
+/*
  * moe_combine -- weighted sum of each token's k expert outputs, back in token
  * order: out[t] = sum_{j=0..k-1} w[t][j] * Y[token_row[t][j]], j ascending, FP32.
  * [LBP] "What W4A4 GEMM Actually Changes" (expert routing); the weights are the

@@ -9,11 +9,15 @@ The entry points carry the names of the C ABI (include/nv4moe.h):
     moe_permute         top-k routing and stable permutation by expert (+ row gather)
     nvfp4_grouped_gemm  grouped NVFP4 x NVFP4 GEMM (GROUP_M with optional SwiGLU, GROUP_K)
     moe_combine         top-k weighted combine back to token order
+    nv4_to_bf16         BF16 operands: BF16-dequantised NVFP4 or BF16, rows / columns
+    bf16_grouped_gemm   the same grouped GEMM on BF16 operands
 
 ``moe_forward`` and ``moe_backward`` compose these calls into the expert layer's
 forward (route, quantise, permute, GEMM + SwiGLU, quantise, GEMM, combine) and
-its four backward grouped GEMMs.  There is no fallback: if the library is not
-built, every call raises.
+its four backward grouped GEMMs.  ``moe_forward_bf16`` is the unquantised layer
+and ``moe_backward_bf16`` the backward on BF16 operands: the forward's NVFP4
+tensors dequantised (the dequantized backward) or the BF16 tensors themselves.
+There is no fallback: if the library is not built, every call raises.
 """
 
 from __future__ import annotations
@@ -68,6 +72,9 @@ _SIGS = {
     "nvfp4_grouped_gemm": (_I, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _P, _I, _I64, _I64, _P,
                                 _I, _I, _P, _I, _I64, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I64, _I, _I64, _P, _I, _P]),
+    "nv4_to_bf16": (_I, [_P, _I64, _I64, ctypes.POINTER(NV4Tensor), _I64, _I64, _P, _I, _I, _P, _P, _P, _I64, _I64,
+                         _P]),
+    "bf16_grouped_gemm": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P, _P]),
 }
 
 
@@ -514,4 +521,206 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
     with _Stage(stage_events, "wgrad_w13", st):
         nvfp4_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
                            stream=stream)
+    return bufs
+
+
+# ----------------------------------------------------------------------------- BF16 operands
+
+def cols_capacity_bf16(R: int, E: int) -> int:
+    """Column capacity of a BF16 column operand (a multiple of 32, the BF16 GEMM's stage)."""
+    return cols_capacity(R, E)
+
+
+def nv4_to_bf16(src, layout: int = NV4_ROWS, nseg: int = 1, seg_offsets: torch.Tensor | None = None,
+                seg_padded_offsets: torch.Tensor | None = None, row_index: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, out_cols: int | None = None, stream=None) -> torch.Tensor:
+    """A BF16 operand from `src`: a 2-D BF16 tensor, or an NVFP4 tensor whose
+    BF16-dequantised values are taken.  NV4_ROWS gives [rows, K]; NV4_COLS the
+    segment transpose [K, cap] (segments zero-padded to 16); NV4_COLS_BATCHED the
+    per-matrix transposes [nseg*K, rows/nseg].  With row_index, logical row r is
+    source row row_index[r]."""
+    lib = load()
+    if isinstance(src, NVFP4):
+        q, x, x_rows, ldx = src.c(), None, 0, 0
+        src_rows, K, device = src.rows, src.K, src.codes.device
+    else:
+        assert src.dim() == 2 and src.stride(1) == 1 and src.dtype == torch.bfloat16
+        q, x, x_rows, ldx = None, src, src.shape[0], src.stride(0)
+        src_rows, K, device = src.shape[0], src.shape[1], src.device
+    rows = row_index.numel() if row_index is not None else src_rows
+    if layout == NV4_ROWS:
+        shape = (rows, K)
+    elif layout == NV4_COLS:
+        shape = (K, out_cols if out_cols is not None else cols_capacity_bf16(rows, nseg))
+    else:
+        shape = (nseg * K, rows // nseg)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    assert out.dtype == torch.bfloat16 and out.is_contiguous()
+    _check(lib.nv4_to_bf16(_ptr(x), x_rows, ldx, None if q is None else ctypes.byref(q), rows, K, _ptr(row_index),
+                           layout, nseg, _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(out), out.shape[0],
+                           out.shape[1], _stream(stream)))
+    return out
+
+
+def bf16_grouped_gemm(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, E: int, N: int,
+                      M_cap: int | None = None, a_rows: torch.Tensor | None = None, group_mode: int = NV4_GROUP_M,
+                      epilogue: int = NV4_EPI_NONE, out_dtype=torch.float32, C: torch.Tensor | None = None,
+                      amax_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_grouped_gemm on BF16 operands A [a_rows, K] and B [b_rows, K] (K contiguous)."""
+    lib = load()
+    for t in (A, B):
+        assert t.dtype == torch.bfloat16 and t.dim() == 2 and t.is_contiguous()
+    K = A.shape[1]
+    assert B.shape[1] == K
+    if group_mode == NV4_GROUP_M:
+        if M_cap is None:
+            M_cap = A.shape[0]
+        if C is None:
+            C = torch.empty((M_cap, N), dtype=out_dtype, device=A.device)
+        ldc = C.stride(0)
+    else:
+        N = A.shape[0]
+        if C is None:
+            C = torch.empty((E, A.shape[0], B.shape[0]), dtype=out_dtype, device=A.device)
+        ldc = C.stride(1)
+        M_cap = 0
+    _check(lib.bf16_grouped_gemm(_ptr(A), A.shape[0], _ptr(B), B.shape[0], K, _ptr(offsets), E, M_cap, N,
+                                 _ptr(a_rows), group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out),
+                                 _stream(stream)))
+    return C
+
+
+# ----------------------------------------------------------------------------- BF16 layer and backward
+
+@dataclass
+class BF16TransposedWeights:
+    """BF16 expert weights transposed for the data gradients: W2^T [E*I, H] and
+    W13^T [E*H, 2I] (either the BF16 weights or the BF16 values of their NVFP4
+    forward form)."""
+    w2t: torch.Tensor
+    w13t: torch.Tensor
+
+
+def bf16_expert_weights_t(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> BF16TransposedWeights:
+    """Transposes of the BF16 weights W13 [E, 2I, H] and W2 [E, H, I]."""
+    E, I2, H = W13.shape
+    w2t = nv4_to_bf16(W2.reshape(E * H, I2 // 2), layout=NV4_COLS_BATCHED, nseg=E, stream=stream)
+    w13t = nv4_to_bf16(W13.reshape(E * I2, H), layout=NV4_COLS_BATCHED, nseg=E, stream=stream)
+    return BF16TransposedWeights(w2t, w13t)
+
+
+def dequantize_expert_weights_t(w: ExpertWeights, stream=None) -> BF16TransposedWeights:
+    """Transposes of the BF16-dequantised NVFP4 weights of the forward (DQ(Q(W)))."""
+    w2t = nv4_to_bf16(w.w2, layout=NV4_COLS_BATCHED, nseg=w.E, stream=stream)
+    w13t = nv4_to_bf16(w.w13, layout=NV4_COLS_BATCHED, nseg=w.E, stream=stream)
+    return BF16TransposedWeights(w2t, w13t)
+
+
+@dataclass
+class BF16ForwardBuffers:
+    hact: torch.Tensor      # [R, I] BF16
+    y: torch.Tensor         # [R, H] FP32
+    out: torch.Tensor       # [T, H]
+    pws: torch.Tensor
+    routing: Routing | None = None
+
+
+def alloc_forward_bf16(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat16,
+                       device="cuda") -> BF16ForwardBuffers:
+    lib = load()
+    R = T * k
+    return BF16ForwardBuffers(hact=torch.empty((R, I), dtype=torch.bfloat16, device=device),
+                              y=torch.empty((R, H), dtype=torch.float32, device=device),
+                              out=torch.empty((T, H), dtype=out_dtype, device=device),
+                              pws=torch.empty(lib.moe_permute_workspace(T, E, k), dtype=torch.uint8, device=device))
+
+
+def moe_forward_bf16(x: torch.Tensor, logits: torch.Tensor, W13: torch.Tensor, W2: torch.Tensor, k: int,
+                     bufs: BF16ForwardBuffers | None = None, stream=None,
+                     stage_events: list | None = None) -> BF16ForwardBuffers:
+    """The unquantised expert layer: W13 [E, 2I, H], W2 [E, H, I] in BF16; the same
+    routing, permutation, SwiGLU and combine as ``moe_forward``."""
+    T, H = x.shape
+    E, I2, _ = W13.shape
+    I = I2 // 2
+    if bufs is None:
+        bufs = alloc_forward_bf16(T, H, E, k, I, device=x.device)
+    R = T * k
+    st = stream if stream is not None else torch.cuda.current_stream()
+    with _Stage(stage_events, "route_permute", st):
+        bufs.routing = moe_permute(logits, E, k, ws=bufs.pws, stream=stream, out=bufs.routing)
+    with _Stage(stage_events, "gemm1_swiglu", st):
+        bf16_grouped_gemm(x, W13.reshape(E * I2, H), bufs.routing.offsets, E, I, M_cap=R,
+                          a_rows=bufs.routing.row_token, epilogue=NV4_EPI_SWIGLU, C=bufs.hact, stream=stream)
+    with _Stage(stage_events, "gemm2", st):
+        bf16_grouped_gemm(bufs.hact, W2.reshape(E * H, I), bufs.routing.offsets, E, H, M_cap=R, C=bufs.y,
+                          stream=stream)
+    with _Stage(stage_events, "combine", st):
+        moe_combine(bufs.y, bufs.routing.token_row, bufs.routing.topk_w, out=bufs.out, stream=stream)
+    return bufs
+
+
+@dataclass
+class BF16BackwardBuffers:
+    dhact: torch.Tensor     # [R, I]
+    dxperm: torch.Tensor    # [R, H]
+    dy2c: torch.Tensor      # [H, Kcap] BF16
+    hc: torch.Tensor        # [I, Kcap]
+    dy13c: torch.Tensor     # [2I, Kcap]
+    xc: torch.Tensor        # [H, Kcap]
+    dw2: torch.Tensor       # [E, H, I]
+    dw13: torch.Tensor      # [E, 2I, H]
+
+
+def alloc_backward_bf16(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfloat16,
+                        wgrad_dtype=torch.float32, device="cuda") -> BF16BackwardBuffers:
+    R = T * k
+    kc = cols_capacity_bf16(R, E)
+    b = lambda r: torch.empty((r, kc), dtype=torch.bfloat16, device=device)
+    return BF16BackwardBuffers(
+        dhact=torch.empty((R, I), dtype=dgrad_dtype, device=device),
+        dxperm=torch.empty((R, H), dtype=dgrad_dtype, device=device),
+        dy2c=b(H), hc=b(I), dy13c=b(2 * I), xc=b(H),
+        dw2=torch.empty((E, H, I), dtype=wgrad_dtype, device=device),
+        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device))
+
+
+def moe_backward_bf16(x_op, hact_op, wt: BF16TransposedWeights, dY2: torch.Tensor, dY13: torch.Tensor,
+                      routing: Routing, bufs: BF16BackwardBuffers | None = None, stream=None,
+                      stage_events: list | None = None) -> BF16BackwardBuffers:
+    """The four backward grouped GEMMs of ``moe_backward`` on BF16 operands, with
+    the upstream gradients dY2 [R, H] and dY13 [R, 2I] (expert row order) in BF16.
+
+    x_op is X [T, H] in BF16 or the forward's NVFP4 X; hact_op is the SwiGLU output
+    [R, I] in BF16 or the forward's NVFP4 form of it.  An NVFP4 operand enters as
+    its BF16-dequantised values: with the forward's NVFP4 tensors and
+    ``dequantize_expert_weights_t`` this is the dequantized backward; with the
+    BF16 tensors and ``bf16_expert_weights_t`` the BF16 backward."""
+    rt = routing
+    E = rt.offsets.numel() - 1
+    R = rt.row_token.numel()
+    H = dY2.shape[1]
+    I = dY13.shape[1] // 2
+    T = x_op.rows if isinstance(x_op, NVFP4) else x_op.shape[0]
+    if bufs is None:
+        bufs = alloc_backward_bf16(T, H, E, R // T, I, device=dY2.device)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    seg = dict(layout=NV4_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets, stream=stream)
+    with _Stage(stage_events, "dgrad_hact", st):
+        bf16_grouped_gemm(dY2, wt.w2t, rt.offsets, E, I, M_cap=R, C=bufs.dhact, stream=stream)
+    with _Stage(stage_events, "dgrad_x", st):
+        bf16_grouped_gemm(dY13, wt.w13t, rt.offsets, E, H, M_cap=R, C=bufs.dxperm, stream=stream)
+    with _Stage(stage_events, "cols_dy2_hact", st):
+        nv4_to_bf16(dY2, out=bufs.dy2c, **seg)
+        nv4_to_bf16(hact_op, out=bufs.hc, **seg)
+    with _Stage(stage_events, "wgrad_w2", st):
+        bf16_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
+                          stream=stream)
+    with _Stage(stage_events, "cols_dy13_x", st):
+        nv4_to_bf16(dY13, out=bufs.dy13c, **seg)
+        nv4_to_bf16(x_op, out=bufs.xc, row_index=rt.row_token, **seg)
+    with _Stage(stage_events, "wgrad_w13", st):
+        bf16_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
+                          stream=stream)
     return bufs

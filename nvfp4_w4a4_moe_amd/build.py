@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libnv4moe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("NV4_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["quantize.hip", "permute.hip", "gemm.hip", "combine.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "permute.hip", "gemm.hip", "convert.hip", "combine.hip", "api.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

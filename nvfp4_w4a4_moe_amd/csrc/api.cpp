@@ -345,6 +345,131 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
   return from_hip(nv4::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)), "nvfp4_grouped_gemm");
 }
 
+nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int64_t b_rows_n, int64_t K,
+                             const int32_t *offsets, int E, int64_t M_cap, int64_t N, const int32_t *a_rows,
+                             int group_mode, int epilogue, void *C, nv4_dtype ctype, int64_t ldc,
+                             float *amax_out, void *stream) {
+  if (!A || !B || !offsets || !C) return fail(NV4_EINVAL, "bf16_grouped_gemm: NULL argument");
+  if (E <= 0 || E > 1024) return fail(NV4_EINVAL, "bf16_grouped_gemm: E must be in [1, 1024]");
+  if (group_mode != NV4_GROUP_M && group_mode != NV4_GROUP_K)
+    return fail(NV4_EINVAL, "bf16_grouped_gemm: bad group_mode");
+  if (epilogue != NV4_EPI_NONE && epilogue != NV4_EPI_SWIGLU)
+    return fail(NV4_EINVAL, "bf16_grouped_gemm: bad epilogue");
+  if (ctype != NV4_BF16 && ctype != NV4_F32) return fail(NV4_EINVAL, "bf16_grouped_gemm: bad C dtype");
+  if (K <= 0 || K % 32)
+    return fail(NV4_EALIGN, "bf16_grouped_gemm: K = %lld must be a positive multiple of 32", (long long)K);
+  if (!aligned(A, 16) || !aligned(B, 16)) return fail(NV4_EALIGN, "bf16_grouped_gemm: A and B must be 16-byte aligned");
+  // the kernel addresses operands with 32-bit byte offsets and C with 32-bit element offsets
+  if (a_rows_n < 0 || b_rows_n < 0 || a_rows_n * K * 2 >= (1ll << 32) || b_rows_n * K * 2 >= (1ll << 32))
+    return fail(NV4_EINVAL, "bf16_grouped_gemm: each operand must stay below 4 GiB");
+  nv4::GemmArgs g{};
+  g.operands_bf16 = 1;
+  g.a_codes = static_cast<const uint8_t *>(A);
+  g.a_scale_mode = NV4_SCALE_TENSOR;
+  g.a_rows = a_rows_n;
+  g.K = K;
+  g.a_rows_index = a_rows;
+  g.b_codes = static_cast<const uint8_t *>(B);
+  g.b_scale_mode = NV4_SCALE_TENSOR;
+  g.b_rows = b_rows_n;
+  g.offsets = offsets;
+  g.E = E;
+  g.M_cap = M_cap;
+  g.N = N;
+  g.group_mode = group_mode;
+  g.epilogue = epilogue;
+  g.C = C;
+  g.c_is_f32 = ctype == NV4_F32;
+  g.ldc = ldc;
+  g.amax_out = amax_out;
+  if (group_mode == NV4_GROUP_M) {
+    const int64_t Nb = epilogue == NV4_EPI_SWIGLU ? 2 * N : N;
+    if (N <= 0) return fail(NV4_EINVAL, "bf16_grouped_gemm: N must be positive");
+    if (b_rows_n != (int64_t)E * Nb)
+      return fail(NV4_EINVAL, "bf16_grouped_gemm: B has %lld rows, expected E * %lld", (long long)b_rows_n,
+                  (long long)Nb);
+    if (M_cap < 0 || (a_rows == nullptr && M_cap > a_rows_n))
+      return fail(NV4_EINVAL, "bf16_grouped_gemm: M_cap exceeds the rows of A");
+    if (ldc < N) return fail(NV4_EINVAL, "bf16_grouped_gemm: ldc < N");
+    if (M_cap * ldc >= (1ll << 31)) return fail(NV4_EINVAL, "bf16_grouped_gemm: C must stay below 2^31 elements");
+  } else {
+    if (epilogue != NV4_EPI_NONE) return fail(NV4_EUNSUPPORTED, "bf16_grouped_gemm: GROUP_K has no SwiGLU epilogue");
+    if (a_rows) return fail(NV4_EUNSUPPORTED, "bf16_grouped_gemm: GROUP_K takes no row index");
+    if (ldc < b_rows_n) return fail(NV4_EINVAL, "bf16_grouped_gemm: ldc < rows of B");
+    if ((int64_t)E * a_rows_n * ldc >= (1ll << 31))
+      return fail(NV4_EINVAL, "bf16_grouped_gemm: C must stay below 2^31 elements");
+    g.N = b_rows_n;
+  }
+  return from_hip(nv4::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)), "bf16_grouped_gemm");
+}
+
+// ---------------------------------------------------------------- BF16 operands
+
+nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_tensor *q, int64_t rows, int64_t K,
+                       const int32_t *row_index, int layout, int nseg, const int32_t *seg_offsets,
+                       const int32_t *seg_padded_offsets, void *out, int64_t out_rows, int64_t out_cols,
+                       void *stream) {
+  if ((x == nullptr) == (q == nullptr)) return fail(NV4_EINVAL, "nv4_to_bf16: give exactly one of x and q");
+  if (!out) return fail(NV4_EINVAL, "nv4_to_bf16: NULL out");
+  if (rows < 0 || K <= 0) return fail(NV4_EINVAL, "nv4_to_bf16: bad shape");
+  if (K % 16) return fail(NV4_EALIGN, "nv4_to_bf16: K must be a multiple of 16");
+  if (!aligned(out, 16)) return fail(NV4_EALIGN, "nv4_to_bf16: out must be 16-byte aligned");
+  nv4::ConvertArgs a{};
+  if (x) {
+    if (ldx < K || ldx % 8) return fail(NV4_EALIGN, "nv4_to_bf16: ldx must be >= K and a multiple of 8");
+    if (!aligned(x, 16)) return fail(NV4_EALIGN, "nv4_to_bf16: x must be 16-byte aligned");
+    if (x_rows < 0 || (!row_index && x_rows != rows)) return fail(NV4_EINVAL, "nv4_to_bf16: x_rows != rows");
+    if (row_index && rows > 0 && x_rows == 0) return fail(NV4_EINVAL, "nv4_to_bf16: row index into an empty x");
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.src_rows = x_rows;
+  } else {
+    if (!q->codes || !q->scales || !q->tscale) return fail(NV4_EINVAL, "nv4_to_bf16: NULL tensor buffer");
+    if (q->K != K) return fail(NV4_EINVAL, "nv4_to_bf16: q->K != K");
+    if (!aligned(q->codes, 8)) return fail(NV4_EALIGN, "nv4_to_bf16: codes must be 8-byte aligned");
+    if (!row_index && q->rows != rows) return fail(NV4_EINVAL, "nv4_to_bf16: q->rows != rows");
+    if (row_index && rows > 0 && q->rows <= 0) return fail(NV4_EINVAL, "nv4_to_bf16: row index into an empty q");
+    if (q->scale_mode == NV4_SCALE_SEGMENT && (q->nseg <= 0 || q->rows % q->nseg))
+      return fail(NV4_EINVAL, "nv4_to_bf16: segment scales need q->rows % q->nseg == 0");
+    if (q->scale_mode != NV4_SCALE_TENSOR && q->scale_mode != NV4_SCALE_SEGMENT && q->scale_mode != NV4_SCALE_ROW)
+      return fail(NV4_EINVAL, "nv4_to_bf16: bad q->scale_mode");
+    a.codes = q->codes;
+    a.scales = q->scales;
+    a.tscale = q->tscale;
+    a.scale_mode = q->scale_mode;
+    a.src_rows = q->rows;
+    a.src_nseg = q->nseg;
+  }
+  a.rows = rows;
+  a.K = K;
+  a.row_index = row_index;
+  a.layout = layout;
+  a.nseg = nseg;
+  a.seg_offsets = seg_offsets;
+  a.seg_padded_offsets = seg_padded_offsets;
+  a.out = static_cast<uint16_t *>(out);
+  a.out_rows = out_rows;
+  a.out_cols = out_cols;
+  if (layout == NV4_ROWS) {
+    if (out_rows != rows || out_cols != K) return fail(NV4_EINVAL, "nv4_to_bf16: ROWS output must be [rows][K]");
+  } else if (layout == NV4_COLS) {
+    if (nseg < 1 || nseg > (1 << 20) || !seg_offsets || !seg_padded_offsets)
+      return fail(NV4_EINVAL, "nv4_to_bf16: COLS needs nseg >= 1 and both offset arrays");
+    if (out_rows != K) return fail(NV4_EINVAL, "nv4_to_bf16: COLS output must have K rows");
+    if (out_cols < rows + 15 * (int64_t)nseg || out_cols % 8)
+      return fail(NV4_EINVAL, "nv4_to_bf16: COLS output needs >= rows + 15 * nseg columns, a multiple of 8");
+  } else if (layout == NV4_COLS_BATCHED) {
+    if (row_index) return fail(NV4_EUNSUPPORTED, "nv4_to_bf16: COLS_BATCHED takes no row index");
+    if (nseg < 1 || nseg > 65535 || rows % nseg || (rows / nseg) % 16)
+      return fail(NV4_EINVAL, "nv4_to_bf16: COLS_BATCHED needs rows / nseg a multiple of 16");
+    if (out_rows != (int64_t)nseg * K || out_cols != rows / nseg)
+      return fail(NV4_EINVAL, "nv4_to_bf16: COLS_BATCHED output must be [nseg * K][rows / nseg]");
+  } else {
+    return fail(NV4_EINVAL, "nv4_to_bf16: bad layout");
+  }
+  return from_hip(nv4::launch_convert(a, static_cast<hipStream_t>(stream)), "nv4_to_bf16");
+}
+
 // ---------------------------------------------------------------- combine
 
 nv4_status moe_combine(const void *Y, nv4_dtype ytype, int64_t ldy, const int32_t *token_row,

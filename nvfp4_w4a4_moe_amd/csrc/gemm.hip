@@ -25,6 +25,15 @@
 // one 16-byte LDS read gives a lane all 32 codes it needs for the slice.  Any
 // permutation of K applied to both operands leaves the dot product unchanged.
 //
+// BF16 operands (the unquantised layer and the BF16 / dequantized backward of
+// "The 4-bitter Lesson", section "Improving Gradient Stability") use the same
+// kernel with the decode removed: stages of 32 BF16 elements (64 bytes per row,
+// the same LDS layout as a stage of 128 FP4 codes), one 16-byte LDS read per
+// fragment row per MFMA step, v_mfma_f32_32x32x16_bf16, no tensor scales.  BF16
+// reads 4x the operand bytes of FP4 per MFMA, so it runs 128 x 128 wave tiles
+// (one wave per SIMD, accumulators in the AGPR half of the register file) to
+// keep the LDS traffic per MFMA down.
+//
 // Tile order: the logical tile index is split so that the workgroups of one XCD
 // (hardware assigns workgroup i to XCD i % 8) take consecutive tiles, which share
 // the A rows (same M tile) and the expert's B matrix in that XCD's L2.
@@ -40,17 +49,20 @@ namespace {
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;
 
-template <int WAVES_M, int WAVES_N, int FM, int FN, int WAVES_PER_SIMD = 1, int STAGES = 2>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int WAVES_M, int WAVES_N, int FM, int FN, int WAVES_PER_SIMD = 1, int STAGES = 2, bool BF16 = false>
 struct TileCfg {
+  static constexpr bool kBf16 = BF16;                   // operands BF16 (else NVFP4)
   static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N, kFM = FM, kFN = FN;
   static constexpr int kWavesPerSimd = WAVES_PER_SIMD;  // occupancy the registers are budgeted for
   static constexpr int kStages = STAGES;                // LDS ring depth (prefetch distance STAGES - 1)
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;  // rows of B per tile
-  static constexpr int BK = 128;                // K per LDS stage
+  static constexpr int BK = BF16 ? 32 : 128;    // K per LDS stage
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
-  static constexpr int kRowBytes = BK / 2;      // packed codes per row per stage
-  static constexpr int kScBytes = BK / 16;      // scale bytes per row per stage
+  static constexpr int kRowBytes = BF16 ? BK * 2 : BK / 2;  // element bytes per row per stage (64)
+  static constexpr int kScBytes = BF16 ? 0 : BK / 16;       // scale bytes per row per stage
   static constexpr int kStageBytes = (BM + BN) * (kRowBytes + kScBytes);
 };
 
@@ -215,9 +227,10 @@ void k_gemm(GemmArgs g) {
   constexpr int RB = Cfg::kRowBytes, SB = Cfg::kScBytes;
   // LDS DMA plan: codes in 1 KB blocks of 16 rows, scales in 256-byte blocks of 32
   // rows (A rows first, then B rows); wave w issues blocks w, w + NW, ...
-  constexpr int kCodeBlocks = (BM + BN) / 16, kScBlocks = (BM + BN) / 32;
+  constexpr bool BF = Cfg::kBf16;
+  constexpr int kCodeBlocks = (BM + BN) / 16, kScBlocks = BF ? 0 : (BM + BN) / 32;
   constexpr int kCodeIters = (kCodeBlocks + NW - 1) / NW;
-  constexpr int kScIters = (kScBlocks + NW - 1) / NW;
+  constexpr int kScIters = BF ? 1 : (kScBlocks + NW - 1) / NW;
   // DMAs every wave issues per stage (the vmcnt wait uses the smallest count)
   constexpr int kDmaMin = kCodeBlocks / NW + kScBlocks / NW;
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows must be multiples of 32");
@@ -240,7 +253,7 @@ void k_gemm(GemmArgs g) {
   const int h = lane >> 5, l32 = lane & 31;
   const int E = g.E;
   const int64_t K = g.K;
-  const int64_t ldA = K >> 1, ldAs = K >> 4;  // bytes per row: codes, scales
+  const int64_t ldA = BF ? K * 2 : K >> 1, ldAs = K >> 4;  // bytes per row: elements (codes), scales
   // buffer resources: loads past num_records return zeros (operands are < 4 GiB)
   const uint32_t na_c = (uint32_t)(g.a_rows * ldA), na_s = (uint32_t)(g.a_rows * ldAs);
   const uint32_t nb_c = (uint32_t)(g.b_rows * ldA), nb_s = (uint32_t)(g.b_rows * ldAs);
@@ -263,7 +276,7 @@ void k_gemm(GemmArgs g) {
   const int per_xcd = G / kXcds;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
 
-  const float a_ts = (!A_ROW_SCALE) ? g.a_tscale[0] : 1.0f;
+  const float a_ts = (!A_ROW_SCALE && !Cfg::kBf16) ? g.a_tscale[0] : 1.0f;
   float amax_run = 0.0f;
 
   for (int64_t it = 0;; ++it) {
@@ -335,7 +348,7 @@ void k_gemm(GemmArgs g) {
     }
     uint32_t s_off[kScIters];
 #pragma unroll
-    for (int j = 0; j < kScIters; ++j) {
+    for (int j = 0; j < (BF ? 0 : kScIters); ++j) {
       const int row = (j * NW + wave) * 32 + (lane >> 1);
       const bool isA = row < BM;
       const int r = isA ? row : row - BM;
@@ -350,7 +363,8 @@ void k_gemm(GemmArgs g) {
     const int nk = job.k_hi > job.k_lo ? (int)((job.k_hi - kb0 + BK - 1) / BK) : 0;
 
     auto issue = [&](int kt, uint8_t *dst) {
-      const uint32_t kc = (uint32_t)((kb0 + (int64_t)kt * BK) >> 1);  // code byte offset of the stage
+      // element (code) byte offset of the stage
+      const uint32_t kc = (uint32_t)(BF ? (kb0 + (int64_t)kt * BK) * 2 : (kb0 + (int64_t)kt * BK) >> 1);
       const uint32_t ks = (uint32_t)((kb0 + (int64_t)kt * BK) >> 4);  // scale byte offset of the stage
 #pragma unroll
       for (int j = 0; j < kCodeIters; ++j) {
@@ -364,7 +378,7 @@ void k_gemm(GemmArgs g) {
         else dma16_to_lds(g.b_codes, nb_c, dst + blk * 1024, c_off[j] + kc);
       }
 #pragma unroll
-      for (int j = 0; j < kScIters; ++j) {
+      for (int j = 0; j < (BF ? 0 : kScIters); ++j) {
         const int blk = j * NW + wave;
         if (kScBlocks % NW != 0 && blk >= kScBlocks) break;
         const bool isA = blk * 32 < BM;
@@ -384,7 +398,7 @@ void k_gemm(GemmArgs g) {
     // LDS stage layout: per 64-wide K slice ("sub"), every fragment row reads 32
     // codes (one 16-byte LDS read) and two scale bytes; MFMA step t = sub*4 + s
     // consumes dword s of those codes with the scale of block s/2.
-    constexpr int kSubs = BK / 64, kSteps = BK / 16;
+    constexpr int kSubs = BF ? 1 : BK / 64, kSteps = BK / 16;  // (NVFP4 only)
     uint4 ca[kSubs][FM], cb[kSubs][FN];
     f16x2 sa[kSubs][FM], sbv[kSubs][FN];
     auto lds_read = [&](int sub, const uint8_t *base, int kt) {
@@ -438,6 +452,45 @@ void k_gemm(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     };
+    // BF16: MFMA step t of a stage takes 16 elements; lane half h supplies
+    // elements t*16 + h*8 + [0, 8), 16-byte chunk 2t + h of the row.  An 8-element
+    // group outside [k_lo, k_hi) is zeroed in both operands (ranges are 16-aligned,
+    // so a group is either wholly inside or wholly outside).
+    auto bf16_stage = [&](const uint8_t *base, int kt) {
+      const int64_t k0 = kb0 + (int64_t)kt * BK;
+      const bool full = k0 >= job.k_lo && k0 + BK <= job.k_hi;
+      constexpr int kStepsBf = BK / 16;
+#pragma unroll
+      for (int t = 0; t < kStepsBf; ++t) {
+        bf16x8 av[FM], bv[FN];
+        const int q = 2 * t + h;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * FM * 32 + i * 32 + l32;
+          av[i] = *reinterpret_cast<const bf16x8 *>(base + row * RB + swz(q, row) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * FN * 32 + j * 32 + l32;
+          bv[j] = *reinterpret_cast<const bf16x8 *>(base + BM * RB + row * RB + swz(q, row) * 16);
+        }
+        if (!full) {
+          const int64_t kb = k0 + t * 16 + h * 8;
+          if (!(kb >= job.k_lo && kb < job.k_hi)) {
+            const bf16x8 z = {};
+#pragma unroll
+            for (int i = 0; i < FM; ++i) av[i] = z;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bv[j] = z;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    };
     // wait until this wave's LDS DMA of stage `need` is done, given that `after`
     // more stages were issued after it
     auto wait_stage = [&](int after) {
@@ -457,13 +510,17 @@ void k_gemm(GemmArgs g) {
         block_barrier();
         if (kt + S - 1 < nk) issue(kt + S - 1, bufp((B + S - 1) % S));
         const uint8_t *base = bufp(B);
+        if constexpr (BF) {
+          bf16_stage(base, kt);
+        } else {
 #pragma unroll
-        for (int sub = 0; sub < kSubs; ++sub) lds_read(sub, base, kt);
+          for (int sub = 0; sub < kSubs; ++sub) lds_read(sub, base, kt);
 #pragma unroll
-        for (int t = 0; t < kSteps; ++t) {
-          f16x8 av[FM], bv[FN];
-          decode(t, av, bv);
-          mfmas(av, bv);
+          for (int t = 0; t < kSteps; ++t) {
+            f16x8 av[FM], bv[FN];
+            decode(t, av, bv);
+            mfmas(av, bv);
+          }
         }
       };
       for (int kt = 0; kt < nk; kt += S) {
@@ -479,7 +536,8 @@ void k_gemm(GemmArgs g) {
 
     // ---- epilogue: tensor scales, optional SwiGLU, store
     float b_ts = 1.0f;
-    if (GROUP == NV4_GROUP_M) b_ts = g.b_scale_mode == NV4_SCALE_SEGMENT ? g.b_tscale[job.e] : g.b_tscale[0];
+    if (BF) b_ts = 1.0f;
+    else if (GROUP == NV4_GROUP_M) b_ts = g.b_scale_mode == NV4_SCALE_SEGMENT ? g.b_tscale[job.e] : g.b_tscale[0];
     else b_ts = g.b_tscale[0];
     const int ldc = (int)g.ldc;
     int colw, ncols;  // first output column of this wave's fragment 0 (before the lane), column count
@@ -567,21 +625,37 @@ void k_gemm(GemmArgs g) {
 // wave's FP16 decode overlaps the other's MFMAs), double-buffered LDS stages.
 // 128-row tiles keep the padding of ragged expert segments small.
 using GemmTile = TileCfg<1, 4, 4, 2, 2, 2>;
+// BF16 operands: 256 x 256 workgroup tiles of four 128 x 128 wave tiles, one
+// workgroup per CU, a ring of four 32 KB stages (three in flight).
+using GemmTileBf16 = TileCfg<2, 2, 4, 4, 1, 4, true>;
 
-template <int GROUP, int EPI, bool OUT_F32, bool ROWS>
+template <int GROUP, int EPI, bool OUT_F32, bool ROWS, class Cfg = GemmTile>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
-  using Cfg = GemmTile;
   const int cus = device_cu_count();
-  int grid = cus * 2;  // two resident workgroups per CU (LDS and registers allow two)
+  // resident workgroups per CU: two for NVFP4 (LDS and registers allow two), one for BF16
+  int grid = cus * Cfg::kWavesPerSimd * 4 / (Cfg::kThreads / 64);
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   k_gemm<Cfg, GROUP, EPI, OUT_F32, ROWS><<<grid, Cfg::kThreads, 0, stream>>>(g);
   return hipGetLastError();
 }
 
+hipError_t launch_bf16(const GemmArgs &g, hipStream_t stream) {
+  using C = GemmTileBf16;
+  if (g.group_mode == NV4_GROUP_K)
+    return g.c_is_f32 ? launch_tile<NV4_GROUP_K, NV4_EPI_NONE, true, false, C>(g, stream)
+                      : launch_tile<NV4_GROUP_K, NV4_EPI_NONE, false, false, C>(g, stream);
+  if (g.epilogue == NV4_EPI_SWIGLU)
+    return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, true, false, C>(g, stream)
+                      : launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, false, false, C>(g, stream);
+  return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_NONE, true, false, C>(g, stream)
+                    : launch_tile<NV4_GROUP_M, NV4_EPI_NONE, false, false, C>(g, stream);
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmArgs &g, hipStream_t stream) {
+  if (g.operands_bf16) return launch_bf16(g, stream);
   const bool rows = g.a_scale_mode == NV4_SCALE_ROW;
   if (g.group_mode == NV4_GROUP_K) {
     return g.c_is_f32 ? launch_tile<NV4_GROUP_K, NV4_EPI_NONE, true, false>(g, stream)

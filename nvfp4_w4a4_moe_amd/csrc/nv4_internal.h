@@ -70,8 +70,28 @@ struct GemmArgs {
   int c_is_f32;
   int64_t ldc;
   float *amax_out;
+  int operands_bf16;             // 1: a_codes / b_codes hold BF16 elements (no scales)
 };
 hipError_t launch_grouped_gemm(const GemmArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------- BF16 operands
+struct ConvertArgs {
+  const uint16_t *x;                  // BF16 source [.][ldx], or null
+  int64_t ldx;
+  const uint8_t *codes, *scales;      // NVFP4 source, or null
+  const float *tscale;
+  int scale_mode;                     // of the NVFP4 source
+  int64_t src_rows;                   // rows of the source (x or the NVFP4 tensor)
+  int src_nseg;
+  int64_t rows, K;                    // logical rows (after the gather) and columns
+  const int32_t *row_index;           // may be null
+  int layout;                         // NV4_ROWS / NV4_COLS / NV4_COLS_BATCHED
+  int nseg;
+  const int32_t *seg_offsets, *seg_padded_offsets;
+  uint16_t *out;
+  int64_t out_rows, out_cols;
+};
+hipError_t launch_convert(const ConvertArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 struct CombineArgs {

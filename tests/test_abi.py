@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
     assert set(names) == {"nv4_version", "nv4_status_string", "nv4_last_error", "nvfp4_quantize_workspace",
                           "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
-                          "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine"}
+                          "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
+                          "nv4_to_bf16", "bf16_grouped_gemm"}
 
 
 def test_binding_covers_every_symbol():
@@ -119,3 +120,39 @@ def test_combine_validation(lib):
     assert lib.moe_combine(P, 1, 2000, P, P, 16, 8, 2048, P, 0, None) == -2
     assert lib.moe_combine(P, 3, 2048, P, P, 16, 8, 2048, P, 0, None) == -1
     assert lib.moe_combine(ctypes.c_void_p(0x1004), 1, 2048, P, P, 16, 8, 2048, P, 0, None) == -2
+
+
+def test_to_bf16_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    q = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 64, 128, 0, 1)
+    c = lambda x=P, q=None, rows=64, K=128, ldx=128, xr=64, ri=None, layout=1, nseg=1, off=None, po=None, out=P, \
+        orow=64, ocol=128: lib.nv4_to_bf16(x, xr, ldx, None if q is None else ctypes.byref(q), rows, K, ri, layout,
+                                           nseg, off, po, out, orow, ocol, None)
+    assert c(x=None) == -1                       # neither source
+    assert c(q=q) == -1                          # both sources
+    assert c(K=120, ldx=120, ocol=120) == -2     # K % 16
+    assert c(ldx=132) == -2                      # ldx % 8
+    assert c(x=ctypes.c_void_p(0x1008)) == -2    # x misaligned
+    assert c(orow=63) == -1                      # rows output shape
+    assert c(xr=65) == -1                        # x rows != rows without a gather
+    assert c(layout=2, nseg=4, orow=128, ocol=64 + 15 * 4 + 4) == -1      # COLS without offsets
+    assert c(layout=2, nseg=4, off=P, po=P, orow=128, ocol=120) == -1      # COLS capacity
+    assert c(layout=3, nseg=3, orow=3 * 128, ocol=21) == -1               # batched rows / nseg % 16
+    assert c(layout=3, nseg=2, ri=P, orow=256, ocol=32) == -3             # no gather when batched
+    assert c(layout=9) == -1
+    assert b"layout" in lib.nv4_last_error()
+
+
+def test_bf16_gemm_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    g = lambda A=P, ar=256, B=P, br=8 * 1536, K=2048, E=8, Mc=256, N=768, ri=None, mode=0, epi=1, ldc=768: \
+        lib.bf16_grouped_gemm(A, ar, B, br, K, P, E, Mc, N, ri, mode, epi, P, 1, ldc, None, None)
+    assert g(K=2040) == -2                       # K % 32
+    assert g(A=ctypes.c_void_p(0x1008)) == -2    # A misaligned
+    assert g(N=700) == -1                        # B rows != E * 2N
+    assert g(ldc=100) == -1
+    assert g(Mc=257) == -1                       # M_cap > rows of A
+    assert g(mode=1) == -3                       # SwiGLU with GROUP_K
+    assert g(mode=1, epi=0, ri=P, ldc=1536) == -3   # row index with GROUP_K
+    assert g(ar=1 << 20, K=4096, ri=P) == -1     # A above 4 GiB
+    assert g(E=0) == -1

@@ -1,0 +1,243 @@
+"""BF16 operands and the BF16 grouped GEMM on the GPU: the unquantised layer and
+the BF16 / dequantized backward (*The 4-bitter Lesson*, sections "Why is the
+NVFP4 pretraining recipe not sufficient for RL?" and "Improving Gradient
+Stability").
+
+Bars: the BF16 operands (dequantised NVFP4 values, gathers, transposes, zero
+padding) bit for bit against the oracle; every GEMM within 1e-5 relative
+Frobenius error of the oracle's FP64 product of the same BF16 operands; BF16
+outputs equal to the round-to-nearest-even of the FP32 outputs; bitwise
+repeatability."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe
+from oracle import nvfp4 as Q
+from oracle import pipeline
+from tests.gpu_util import bf16_rne_of, dev_bf16, dev_f32, dev_i32, host, nvfp4_host, rel_frob
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _ragged_offsets(R, E, seed, empty=(1,)):
+    """Ragged expert segments summing to R, with the listed experts empty."""
+    r = synth.rng(seed)
+    w = r.uniform(0.2, 2.0, E)
+    w[list(empty)] = 0
+    n = np.floor(w / w.sum() * R).astype(np.int64)
+    n[np.argmax(w)] += R - n.sum()
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+
+def _bf16_vals(shape, seed, std=1.0):
+    return synth.to_bf16_values(synth.rng(seed).standard_normal(shape).astype(np.float32) * std)
+
+
+# ----------------------------------------------------------------------------- operands
+
+@pytest.mark.parametrize("mode", ["tensor", "row", "segment"])
+def test_dequantize_rows_exact(gpu_lib, mode):
+    """nv4_to_bf16 of an NVFP4 tensor (rows) equals the oracle's BF16 dequantisation
+    of the same bytes, for each tensor-scale grouping; K = 80 is not a multiple of 64."""
+    x = synth.activations(300, 80, 5)
+    m = {"tensor": gpu_lib.NV4_SCALE_TENSOR, "row": gpu_lib.NV4_SCALE_ROW, "segment": gpu_lib.NV4_SCALE_SEGMENT}[mode]
+    q = gpu_lib.nvfp4_quantize(dev_bf16(x), scale_mode=m, nseg=3)
+    ref = Q.dequantize_bf16(nvfp4_host(q))
+    got = gpu_lib.nv4_to_bf16(q)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), ref)
+    # and the quantiser's own bytes are the oracle's
+    qr = Q.quantize_rows(x, mode, nseg=3)
+    assert np.array_equal(host(q.codes), qr.packed())
+
+
+def test_columns_of_bf16_and_nvfp4_with_gather_exact(gpu_lib):
+    """Segment transposes (zero-padded to 16 per segment) of a BF16 tensor and of
+    the dequantised NVFP4 tensor, directly and through a row gather; an empty and
+    a 1-row segment included."""
+    R, C, E = 1000, 96, 7
+    off = _ragged_offsets(R, E, 3, empty=(2,))
+    off[4] = off[3] + 1                        # a one-row segment
+    off[5:] = np.maximum(off[5:], off[4])
+    po = moe.transpose_segments(np.zeros((R, 1)), off)[1]
+    x = _bf16_vals((R, C), 4)
+    src = synth.to_bf16_values(synth.rng(5).standard_normal((333, C)).astype(np.float32))
+    gidx = synth.rng(6).integers(0, 333, R).astype(np.int32)
+    d_off, d_po = dev_i32(off), dev_i32(po)
+    seg = dict(layout=gpu_lib.NV4_COLS, nseg=E, seg_offsets=d_off, seg_padded_offsets=d_po)
+    cap = gpu_lib.cols_capacity_bf16(R, E)
+    got = gpu_lib.nv4_to_bf16(dev_bf16(x), **seg)
+    ref, _ = moe.transpose_segments(x, off)
+    assert got.shape == (C, cap)
+    assert np.array_equal(host(got)[:, :po[-1]], ref)
+    got = gpu_lib.nv4_to_bf16(dev_bf16(src), row_index=dev_i32(gidx), **seg)
+    assert np.array_equal(host(got)[:, :po[-1]], moe.transpose_segments(src[gidx], off)[0])
+    q = gpu_lib.nvfp4_quantize(dev_bf16(src), scale_mode=gpu_lib.NV4_SCALE_ROW)
+    got = gpu_lib.nv4_to_bf16(q, row_index=dev_i32(gidx), **seg)
+    deq = Q.dequantize_bf16(nvfp4_host(q))
+    assert np.array_equal(host(got)[:, :po[-1]], moe.transpose_segments(deq[gidx], off)[0])
+
+
+def test_batched_weight_transposes_exact(gpu_lib):
+    """Per-expert transposes of BF16 weights and of the dequantised NVFP4 weights
+    (one scale per expert)."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    bt = gpu_lib.bf16_expert_weights_t(W13, W2)
+    assert np.array_equal(host(bt.w2t), moe.transpose_batched(d["W2"].reshape(E * H, I), E))
+    assert np.array_equal(host(bt.w13t), moe.transpose_batched(d["W13"].reshape(E * 2 * I, H), E))
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    dt = gpu_lib.dequantize_expert_weights_t(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dt.w2t), moe.transpose_batched(Q.dequantize_bf16(nvfp4_host(w.w2)), E))
+    assert np.array_equal(host(dt.w13t), moe.transpose_batched(Q.dequantize_bf16(nvfp4_host(w.w13)), E))
+
+
+# ----------------------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("R,K,N,E", [(1000, 256, 384, 5), (4099, 768, 2048, 9), (40, 64, 96, 3)])
+def test_bf16_gemm_group_m(gpu_lib, R, K, N, E):
+    """Ragged experts (one empty), several tiles and a ragged tail; FP32 and BF16 out."""
+    off = _ragged_offsets(R, E, R + K)
+    A = _bf16_vals((R, K), 1)
+    B = _bf16_vals((E * N, K), 2, 0.05)
+    dA, dB, doff = dev_bf16(A), dev_bf16(B), dev_i32(off)
+    C32 = gpu_lib.bf16_grouped_gemm(dA, dB, doff, E, N)
+    assert rel_frob(host(C32), moe.grouped_gemm_m(A, B, off, E, N)) <= TOL
+    C16 = gpu_lib.bf16_grouped_gemm(dA, dB, doff, E, N, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(C16), bf16_rne_of(host(C32)))
+    again = gpu_lib.bf16_grouped_gemm(dA, dB, doff, E, N)
+    assert torch.equal(C32.view(torch.int32), again.view(torch.int32))
+
+
+def test_bf16_gemm_swiglu_gather(gpu_lib):
+    """Gate/up GEMM with the row gather and the SwiGLU epilogue (FP32 and BF16 out,
+    the BF16 amax of the stored values)."""
+    T, H, I, E, k = 700, 256, 192, 6, 2
+    R = T * k
+    off = _ragged_offsets(R, E, 9)
+    X = _bf16_vals((T, H), 3)
+    rtok = synth.rng(4).integers(0, T, R).astype(np.int32)
+    W13 = _bf16_vals((E * 2 * I, H), 5, 0.05)
+    dX, dW, doff, drt = dev_bf16(X), dev_bf16(W13), dev_i32(off), dev_i32(rtok)
+    h32 = gpu_lib.bf16_grouped_gemm(dX, dW, doff, E, I, M_cap=R, a_rows=drt, epilogue=gpu_lib.NV4_EPI_SWIGLU)
+    ref = moe.swiglu(moe.grouped_gemm_m(X[rtok], W13, off, E, 2 * I))
+    assert rel_frob(host(h32), ref) <= TOL
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    h16 = gpu_lib.bf16_grouped_gemm(dX, dW, doff, E, I, M_cap=R, a_rows=drt, epilogue=gpu_lib.NV4_EPI_SWIGLU,
+                                    out_dtype=torch.bfloat16, amax_out=amax)
+    assert np.array_equal(host(h16), bf16_rne_of(host(h32)))
+    assert host(amax)[0] == np.abs(host(h16)).max()
+
+
+@pytest.mark.parametrize("R,N,M,E", [(1000, 256, 128, 5), (5000, 384, 768, 9)])
+def test_bf16_gemm_group_k(gpu_lib, R, N, M, E):
+    """Weight-gradient form: per-expert contraction over the expert's own rows of
+    column operands built by nv4_to_bf16; an empty expert gives zeros."""
+    off = _ragged_offsets(R, E, R + N, empty=(0, 3))
+    A = _bf16_vals((R, N), 7)
+    B = _bf16_vals((R, M), 8)
+    po = moe.transpose_segments(np.zeros((R, 1)), off)[1]
+    d_off, d_po = dev_i32(off), dev_i32(po)
+    seg = dict(layout=gpu_lib.NV4_COLS, nseg=E, seg_offsets=d_off, seg_padded_offsets=d_po)
+    Ac = gpu_lib.nv4_to_bf16(dev_bf16(A), **seg)
+    Bc = gpu_lib.nv4_to_bf16(dev_bf16(B), **seg)
+    C = gpu_lib.bf16_grouped_gemm(Ac, Bc, d_po, E, N, group_mode=gpu_lib.NV4_GROUP_K)
+    ref = moe.grouped_gemm_k(moe.transpose_segments(A, off)[0], moe.transpose_segments(B, off)[0], po, E)
+    assert rel_frob(host(C), ref) <= TOL
+    assert not host(C[0]).any() and not host(C[3]).any()
+
+
+# ----------------------------------------------------------------------------- layer
+
+def test_bf16_layer_forward_tiny(gpu_lib):
+    """The unquantised layer: routing and permutation exact, GEMM1 + SwiGLU and
+    GEMM2 within 1e-5 of the oracle on the GPU's own stage inputs, combine."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg)
+    E, H, I, R = cfg.E, cfg.H, cfg.I, cfg.R
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    b = gpu_lib.moe_forward_bf16(dev_bf16(d["X"]), dev_f32(d["logits"]), W13, W2, cfg.k)
+    torch.cuda.synchronize()
+    rt = b.routing
+    ref = pipeline.moe_forward_bf16(d["X"], d["logits"], d["W13"], d["W2"], cfg.k)
+    assert np.array_equal(host(rt.row_token), ref["perm"]["row_token"])
+    off = host(rt.offsets)
+    h32 = gpu_lib.bf16_grouped_gemm(dev_bf16(d["X"]), W13.reshape(E * 2 * I, H), rt.offsets, E, I, M_cap=R,
+                                    a_rows=rt.row_token, epilogue=gpu_lib.NV4_EPI_SWIGLU)
+    assert rel_frob(host(h32), ref["Hact"]) <= TOL
+    assert np.array_equal(host(b.hact), bf16_rne_of(host(h32)))
+    y_ref = moe.grouped_gemm_m(host(b.hact), d["W2"].reshape(E * H, I), off, E, H)
+    assert rel_frob(host(b.y), y_ref) <= TOL
+    o32 = gpu_lib.moe_combine(b.y, rt.token_row, rt.topk_w)
+    assert rel_frob(host(o32), moe.combine(host(b.y), host(rt.token_row), host(rt.topk_w))) <= TOL
+    assert np.array_equal(host(b.out), bf16_rne_of(host(o32)))
+    # end to end against the oracle's BF16 layer (same roundings; agreement up to
+    # FP32-vs-FP64 accumulation moving a BF16 rounding of the SwiGLU output)
+    assert rel_frob(host(b.out), ref["out"]) <= 1e-2
+
+
+@pytest.mark.parametrize("recipe", ["dequantized", "bf16"])
+def test_tiny_bf16_backward_stagewise(gpu_lib, recipe):
+    """Backward on BF16 operands after the NVFP4 forward: the forward's NVFP4
+    tensors dequantised (dequantized backward) or the BF16 tensors (baseline).
+    Operands exact, the four GEMMs within 1e-5 of the oracle's gradients."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    x = dev_bf16(d["X"])
+    f = gpu_lib.moe_forward(x, dev_f32(d["logits"]), w, cfg.k)
+    if recipe == "dequantized":
+        wt = gpu_lib.dequantize_expert_weights_t(w)
+        x_op, h_op = f.xq, f.hq
+    else:
+        wt = gpu_lib.bf16_expert_weights_t(W13, W2)
+        x_op, h_op = x, f.hact
+    bufs = gpu_lib.alloc_backward_bf16(cfg.T, H, E, cfg.k, I, dgrad_dtype=torch.float32)
+    b = gpu_lib.moe_backward_bf16(x_op, h_op, wt, dev_bf16(d["dY2"]), dev_bf16(d["dY13"]), f.routing, bufs)
+    torch.cuda.synchronize()
+    # the oracle's gradients from the forward's own tensors (the GPU forward is
+    # bit-exact with the oracle up to the SwiGLU output, which is taken from the GPU)
+    if recipe == "dequantized":
+        fwd = dict(Xq=nvfp4_host(f.xq), Hq=nvfp4_host(f.hq), W13q=nvfp4_host(w.w13), W2q=nvfp4_host(w.w2))
+        ops = pipeline.backward_operands_bf16(d["X"], None, d["W13"], d["W2"], fwd)
+    else:
+        ops = pipeline.backward_operands_bf16(d["X"], host(f.hact), d["W13"], d["W2"])
+    perm = dict(offsets=host(f.routing.offsets).astype(np.int64), row_token=host(f.routing.row_token))
+    g = pipeline.moe_backward_bf16(ops, d["dY2"], d["dY13"], perm)
+    Kp = int(g["padded_offsets"][-1])
+    assert np.array_equal(host(wt.w2t), g["W2t"]) and np.array_equal(host(wt.w13t), g["W13t"])
+    for name in ("dy2c", "hc", "dy13c", "xc"):
+        ref = {"dy2c": g["dY2c"], "hc": g["Hc"], "dy13c": g["dY13c"], "xc": g["Xc"]}[name]
+        assert np.array_equal(host(getattr(b, name))[:, :Kp], ref), name
+    for name, key in (("dhact", "dHact"), ("dxperm", "dXperm"), ("dw2", "dW2"), ("dw13", "dW13")):
+        assert rel_frob(host(getattr(b, name)), g[key]) <= TOL, name
+
+
+def test_bf16_backward_repeatable_and_bf16_dgrad_is_rne(gpu_lib):
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    f = gpu_lib.moe_forward(dev_bf16(d["X"]), dev_f32(d["logits"]), w, cfg.k)
+    wt = gpu_lib.dequantize_expert_weights_t(w)
+    dY2, dY13 = dev_bf16(d["dY2"]), dev_bf16(d["dY13"])
+    b32 = gpu_lib.alloc_backward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, dgrad_dtype=torch.float32)
+    gpu_lib.moe_backward_bf16(f.xq, f.hq, wt, dY2, dY13, f.routing, b32)
+    b16 = gpu_lib.moe_backward_bf16(f.xq, f.hq, wt, dY2, dY13, f.routing)
+    first = [t.clone() for t in (b16.dhact, b16.dxperm, b16.dw2, b16.dw13)]
+    gpu_lib.moe_backward_bf16(f.xq, f.hq, wt, dY2, dY13, f.routing, b16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(b16.dhact), bf16_rne_of(host(b32.dhact)))
+    assert np.array_equal(host(b16.dxperm), bf16_rne_of(host(b32.dxperm)))
+    for a, c in zip(first, (b16.dhact, b16.dxperm, b16.dw2, b16.dw13)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           c.view(torch.int16) if c.dtype == torch.bfloat16 else c.view(torch.int32))
