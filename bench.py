@@ -23,7 +23,13 @@ stream, the roofline of the dominant kernel, and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--config learner_64k]
-                    [--forward-only] [--no-cpu-baseline]
+                    [--forward-only] [--token-scale] [--recipe nvfp4|dequantized|bf16-backward|bf16]
+                    [--no-compare] [--no-cpu-baseline] [--no-graph]
+
+Besides the timed recipe (default: NVFP4 forward and backward), the same step is
+timed for the other recipes of the pages for comparison ("compare"): the BF16
+(unquantised) layer, and the NVFP4 forward with the dequantized or the BF16
+backward.
 """
 
 from __future__ import annotations
@@ -52,7 +58,7 @@ GEMMS = {
 }
 
 
-def hbm_bytes(cfg) -> dict:
+def hbm_bytes(cfg, recipe: str = "nvfp4") -> dict:
     """Algorithmic HBM bytes of the memory-bound kernels (NVFP4: 0.5 B per code and
     1/16 B per scale; BF16 2 B, FP32 4 B)."""
     T, H, I, k, R, E = cfg.T, cfg.H, cfg.I, cfg.k, cfg.R, cfg.E
@@ -71,6 +77,12 @@ def hbm_bytes(cfg) -> dict:
         "quantize_cols_hact": cols(I),
         "quantize_cols_dy13": cols(2 * I),
         "quantize_cols_x": cols(H),
+        # BF16 column operands (read the source, write BF16 [C, kc]); an NVFP4 source
+        # (the dequantized backward) reads codes and scales instead of BF16
+        "cols_dy2_hact": R * H * 2 + H * kc * 2 + R * I * (0.5 + 1 / 16 if recipe == "dequantized" else 2)
+                         + I * kc * 2,
+        "cols_dy13_x": R * 2 * I * 2 + 2 * I * kc * 2 + R * H * (0.5 + 1 / 16 if recipe == "dequantized" else 2)
+                       + H * kc * 2,
     }
 
 
@@ -172,6 +184,126 @@ def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride
                        f"{expert:.2f} s); FP64 numpy, BLAS threads {cores}")}
 
 
+RECIPES = {
+    "nvfp4": "NVFP4 forward and NVFP4 backward (every backward operand re-quantised along its new "
+             "contraction dimension)",
+    "dequantized": "NVFP4 forward, dequantized backward (BF16 GEMMs on the BF16 values of the forward's "
+                   "NVFP4 weights and activations, BF16 upstream gradients)",
+    "bf16-backward": "NVFP4 forward, BF16 backward on the unquantised weights and activations",
+    "bf16": "BF16 (unquantised) forward and backward",
+}
+DTYPES = {
+    "nvfp4": "nvfp4 (e2m1 + e4m3 block scales, fp32 tensor scales) decoded exactly to f16, f16 MFMA, f32 accumulate",
+    "dequantized": "forward nvfp4 decoded exactly to f16 (f16 MFMA); backward bf16 MFMA; f32 accumulate",
+    "bf16-backward": "forward nvfp4 decoded exactly to f16 (f16 MFMA); backward bf16 MFMA; f32 accumulate",
+    "bf16": "bf16 MFMA, f32 accumulate",
+}
+
+
+def time_recipe(nv4, torch, np, cfg, inp, recipe, backward, args, stages: bool) -> dict:
+    """Weights prepared once (timed separately), warm-up, capture of one step into a
+    HIP graph, then exactly `steps` replays timed by the wall clock between two
+    synchronisations; with `stages`, the same steps again eagerly with HIP events
+    around every call on the launch stream."""
+    x, lg, W13, W2, dY2, dY13 = (inp[n] for n in ("x", "lg", "W13", "W2", "dY2", "dY13"))
+    nvfp4_fwd = recipe != "bf16"
+
+    def prep():
+        w = nv4.quantize_expert_weights(W13, W2) if nvfp4_fwd else None
+        wt = None
+        if backward:
+            if recipe == "nvfp4":
+                wt = nv4.quantize_expert_weights_t(W13, W2)
+            elif recipe == "dequantized":
+                wt = nv4.dequantize_expert_weights_t(w)
+            else:
+                wt = nv4.bf16_expert_weights_t(W13, W2)
+        return w, wt
+
+    wq_ms = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        w, wt = prep()
+        e1.record()
+        torch.cuda.synchronize()
+        wq_ms.append(e0.elapsed_time(e1))
+
+    if nvfp4_fwd:
+        fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, token_scale=args.token_scale)
+    else:
+        fb = nv4.alloc_forward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    bb = None
+    if backward:
+        bb = (nv4.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I) if recipe == "nvfp4"
+              else nv4.alloc_backward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I))
+
+    def step(ev=None):
+        if nvfp4_fwd:
+            nv4.moe_forward(x, lg, w, cfg.k, fb, stage_events=ev)
+        else:
+            nv4.moe_forward_bf16(x, lg, W13, W2, cfg.k, fb, stage_events=ev)
+        if not backward:
+            return
+        if recipe == "nvfp4":
+            nv4.moe_backward(x, fb, wt, dY2, dY13, bb, stage_events=ev)
+        elif recipe == "dequantized":
+            nv4.moe_backward_bf16(fb.xq, fb.hq, wt, dY2, dY13, fb.routing, bb, stage_events=ev)
+        else:
+            nv4.moe_backward_bf16(x, fb.hact, wt, dY2, dY13, fb.routing, bb, stage_events=ev)
+
+    print(f"[bench] {recipe}: warm-up {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # the step's launches captured once into a HIP graph (the library allocates
+    # nothing and clears buffers with kernels, so the step is capturable); each
+    # timed step replays it
+    run = step
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+
+    # timed: exactly K steps, synchronised on both sides (wall clock)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] {recipe}: timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    stage_avg = {}
+    if stages:
+        # the same steps again with per-kernel HIP events on the launch stream
+        ev = []
+        for _ in range(args.steps):
+            step(ev)
+        torch.cuda.synchronize()
+        stage_ms = {}
+        for name, a, b in ev:
+            stage_ms.setdefault(name, []).append(a.elapsed_time(b))
+        stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    counts = np.diff(fb.routing.offsets.cpu().numpy())
+    out = {"ms_per_step": ms_step, "stages": stage_avg, "counts": counts, "weight_ms": float(np.median(wq_ms))}
+    del run, fb, bb, w, wt
+    if not args.no_graph:
+        del graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +314,10 @@ def main():
     ap.add_argument("--token-scale", action="store_true",
                     help="per-token FP32 scales for X and the SwiGLU output instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recipe", default="nvfp4", choices=sorted(RECIPES),
+                    help="the step timed for the JSON line (default: NVFP4 forward and backward)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip timing the other recipes (BF16 layer, dequantized and BF16 backward) for comparison")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from Python each step instead of replaying a captured HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -222,66 +358,22 @@ def main():
     dY2 = dev(d["dY2"], torch.bfloat16) if backward else None
     dY13 = dev(d["dY13"], torch.bfloat16) if backward else None
     torch.cuda.synchronize()
+    inputs = dict(x=x, lg=lg, W13=W13, W2=W2, dY2=dY2, dY13=dY13)
 
-    # weight quantisation (once per optimizer step; not part of the step)
-    wq_ms = []
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        w = nv4.quantize_expert_weights(W13, W2)
-        wt = nv4.quantize_expert_weights_t(W13, W2) if backward else None
-        e1.record()
-        torch.cuda.synchronize()
-        wq_ms.append(e0.elapsed_time(e1))
-
-    fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, token_scale=args.token_scale)
-    bb = nv4.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I) if backward else None
-
-    def step(ev=None):
-        nv4.moe_forward(x, lg, w, cfg.k, fb, stage_events=ev)
-        if backward:
-            nv4.moe_backward(x, fb, wt, dY2, dY13, bb, stage_events=ev)
-
-    print(f"[bench] warm-up {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # the step's ~30 launches captured once into a HIP graph (the library allocates
-    # nothing and clears buffers with kernels, so the step is capturable); each
-    # timed step replays it
-    run = step
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-        run = graph.replay
-
-    # timed: exactly K steps, synchronised on both sides (wall clock)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-
-    # the same steps again with per-kernel HIP events on the launch stream
-    ev = []
-    for _ in range(args.steps):
-        step(ev)
-    torch.cuda.synchronize()
-    stage_ms = {}
-    for name, a, b in ev:
-        stage_ms.setdefault(name, []).append(a.elapsed_time(b))
-    stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    res = time_recipe(nv4, torch, np, cfg, inputs, args.recipe, backward, args, stages=True)
+    ms_step, stage_avg, counts = res["ms_per_step"], res["stages"], res["counts"]
+    compare = {}
+    if not args.no_compare:
+        others = ["bf16"] + (["dequantized", "bf16-backward"] if backward else [])
+        for rcp in others:
+            if rcp == args.recipe:
+                continue
+            print(f"[bench] comparison recipe {rcp}", file=sys.stderr, flush=True)
+            r = time_recipe(nv4, torch, np, cfg, inputs, rcp, backward, args, stages=False)
+            compare[rcp] = {"recipe": RECIPES[rcp], "ms_per_step": round(r["ms_per_step"], 4),
+                            "tokens_per_s": round(cfg.T / (r["ms_per_step"] * 1e-3), 1),
+                            "weight_prep_ms": round(r["weight_ms"], 4),
+                            "time_vs_this_recipe": round(r["ms_per_step"] / ms_step, 4)}
 
     rhi = float(cfg.R) * cfg.H * cfg.I
     flops = rhi * (18.0 if backward else 6.0)
@@ -289,7 +381,7 @@ def main():
     tok_s = cfg.T / (ms_step * 1e-3)
     gemm = {n: (m * rhi / (stage_avg[n] * 1e-3) / 1e12, desc) for n, (m, desc) in GEMMS.items() if n in stage_avg}
     dom = max(gemm, key=lambda n: stage_avg[n])   # the GEMM with the largest time per step
-    nbytes = hbm_bytes(cfg)
+    nbytes = hbm_bytes(cfg, args.recipe)
     other = {}
     for n, (tf, desc) in gemm.items():
         if n != dom:
@@ -300,7 +392,8 @@ def main():
             gbs = b / (stage_avg[n] * 1e-3) / 1e9
             other[n] = {"achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "ms": round(stage_avg[n], 4)}
-    counts = np.diff(fb.routing.offsets.cpu().numpy())
+    bf16_stage = args.recipe == "bf16" or (args.recipe != "nvfp4" and dom not in ("gemm1_swiglu", "gemm2"))
+    kernel = gemm[dom][1].replace("k_gemm", "k_gemm (BF16 operands)") if bf16_stage else gemm[dom][1]
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -313,12 +406,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 + e4m3 block scales, fp32 tensor scales) decoded exactly to f16, f16 MFMA, f32 accumulate",
+        "dtype": DTYPES[args.recipe],
         "data": "synthetic (seeded; random-init expert weights N(0,0.02), activations N(0,1) with 0.1% x20 outliers, "
                 "upstream gradients N(0,1e-3))",
         "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE expert layer "
                                f"{'forward + backward' if backward else 'forward'}"
-                               f"{', per-token activation scales' if args.token_scale else ''}",
+                               f"{', per-token activation scales' if args.token_scale else ''}"
+                               f"{'' if args.recipe == 'nvfp4' else ', ' + RECIPES[args.recipe]}",
                    "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "intermediate": cfg.I,
                    "routing": cfg.routing, "expert_load_max": int(counts.max()),
                    "expert_load_min": int(counts.min()), "empty_experts": int((counts == 0).sum()),
@@ -326,13 +420,15 @@ def main():
                    "flops_per_step": flops},
         "launch": "eager" if args.no_graph else "hip_graph",
         "stages_ms": {k: round(v, 4) for k, v in stage_avg.items()},
-        "weight_quantize_ms": round(float(np.median(wq_ms)), 4),
-        "roofline": {"bound": "mfma", "kernel": gemm[dom][1], "stage": dom,
+        "weight_quantize_ms": round(res["weight_ms"], 4),
+        "roofline": {"bound": "mfma", "kernel": kernel, "stage": dom,
                      "achieved": round(gemm[dom][0], 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm[dom][0] / PEAK_F16_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(dom, cfg.name)},
+                     "traffic": measured_traffic(dom, cfg.name) if args.recipe == "nvfp4" else None},
         "other_kernels": other,
     }
+    if compare:
+        rec["compare"] = compare
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(d, cfg, backward)

@@ -241,3 +241,142 @@ def test_bf16_backward_repeatable_and_bf16_dgrad_is_rne(gpu_lib):
     for a, c in zip(first, (b16.dhact, b16.dxperm, b16.dw2, b16.dw13)):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                            c.view(torch.int16) if c.dtype == torch.bfloat16 else c.view(torch.int32))
+
+
+@pytest.mark.parametrize("recipe", ["bf16", "dequantized"])
+def test_captured_graph_replays_match_eager_bf16(gpu_lib, recipe):
+    """The BF16 layer and the dequantized-backward step captured into a HIP graph
+    (as the benchmark times them): every replay, with eager work in between,
+    equals the eager result bit for bit."""
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    x, lg = dev_bf16(d["X"]), dev_f32(d["logits"])
+    dY2, dY13 = dev_bf16(d["dY2"]), dev_bf16(d["dY13"])
+    bb = gpu_lib.alloc_backward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+    if recipe == "bf16":
+        fb = gpu_lib.alloc_forward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+        wt = gpu_lib.bf16_expert_weights_t(W13, W2)
+
+        def step():
+            gpu_lib.moe_forward_bf16(x, lg, W13, W2, cfg.k, fb)
+            gpu_lib.moe_backward_bf16(x, fb.hact, wt, dY2, dY13, fb.routing, bb)
+    else:
+        fb = gpu_lib.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
+        w = gpu_lib.quantize_expert_weights(W13, W2)
+        wt = gpu_lib.dequantize_expert_weights_t(w)
+
+        def step():
+            gpu_lib.moe_forward(x, lg, w, cfg.k, fb)
+            gpu_lib.moe_backward_bf16(fb.xq, fb.hq, wt, dY2, dY13, fb.routing, bb)
+
+    step()
+    torch.cuda.synchronize()
+    Kp = int(fb.routing.padded_offsets[-1])   # column operands: only the segments' range is written
+    outs = lambda: [t.clone() for t in (fb.out, bb.dhact, bb.dxperm, bb.dw2, bb.dw13, bb.xc[:, :Kp], bb.hc[:, :Kp])]
+    ref = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (fb.out, bb.dw2, bb.dxperm, bb.xc):
+            t.fill_(7)           # eager work between replays that the replay must overwrite
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs()):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+
+
+
+def _dq_rows(t, rows) -> np.ndarray:
+    """The oracle's BF16 dequantisation of rows `rows` of a GPU NVFP4 tensor (bytes
+    gathered on the device), with each row's own tensor scale."""
+    rows = np.asarray(rows, np.int64)
+    idx = torch.as_tensor(rows, device=t.codes.device)
+    codes = Q.unpack_codes(host(t.codes.index_select(0, idx)))
+    sc = host(t.scales.index_select(0, idx))
+    G = host(t.tscale).astype(np.float32)
+    if t.scale_mode == gpu_scale_tensor:
+        g = np.full(len(rows), G[0], np.float32)
+    elif t.scale_mode == gpu_scale_segment:
+        g = G[rows // (t.rows // t.nseg)]
+    else:
+        g = G[rows]
+    Gb = np.repeat(g[:, None], sc.shape[1], axis=1)
+    return Q.dequantize_bf16(Q.NVFP4(codes, sc, G, Gb, np.zeros(1, np.float32)))
+
+
+gpu_scale_tensor, gpu_scale_segment = 0, 1   # NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT
+
+
+def test_learner_dequantized_backward_sampled(gpu_lib):
+    """The long-sequence learner batch (65536 tokens, 128 experts with 13 empty and 4
+    hot ones, top-8) through the NVFP4 forward and the dequantized backward, in the
+    launch configuration the benchmark times.  Sampled rows of the BF16 operands
+    bit for bit (transposed weights; column operands of a hot and an ordinary
+    expert); sampled rows of both data gradients and sampled output rows of both
+    weight gradients (a hot, an ordinary and an empty expert) against the oracle's
+    FP64 products of those operands."""
+    cfg = synth.CONFIGS["learner_64k"]
+    E, H, I, R = cfg.E, cfg.H, cfg.I, cfg.R
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    wt = gpu_lib.dequantize_expert_weights_t(w)
+    f = gpu_lib.moe_forward(dev_bf16(d["X"]), dev_f32(d["logits"]), w, cfg.k)
+    bufs = gpu_lib.alloc_backward_bf16(cfg.T, H, E, cfg.k, I, dgrad_dtype=torch.float32)
+    b = gpu_lib.moe_backward_bf16(f.xq, f.hq, wt, dev_bf16(d["dY2"]), dev_bf16(d["dY13"]), f.routing, bufs)
+    torch.cuda.synchronize()
+    rt = f.routing
+    off = host(rt.offsets).astype(np.int64)
+    po = host(rt.padded_offsets).astype(np.int64)
+    counts = np.diff(off)
+    assert (counts == 0).sum() == 13
+    r = synth.rng(17)
+    sel = lambda t, rows: host(t.index_select(0, torch.as_tensor(np.asarray(rows, np.int64), device=t.device)))
+    hot = int(np.argmax(counts))
+    plain = int(np.flatnonzero((counts > 0) & (counts < counts.max()))[0])
+    empty = int(np.flatnonzero(counts == 0)[0])
+    # transposed dequantised weights of sampled experts
+    for e in (hot, plain):
+        assert np.array_equal(sel(wt.w2t, np.arange(e * I, (e + 1) * I)), _dq_rows(w.w2, np.arange(e * H, (e + 1) * H)).T)
+        assert np.array_equal(sel(wt.w13t, np.arange(e * H, (e + 1) * H)),
+                              _dq_rows(w.w13, np.arange(e * 2 * I, (e + 1) * 2 * I)).T)
+    # data gradients on sampled rows
+    rows = np.sort(r.choice(R, 192, replace=False))
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    dy2, dy13 = d["dY2"][rows].astype(np.float64), d["dY13"][rows].astype(np.float64)
+    ref2, ref13 = np.zeros((len(rows), I)), np.zeros((len(rows), H))
+    for e in np.unique(e_of):
+        m = e_of == e
+        ref2[m] = dy2[m] @ sel(wt.w2t, np.arange(e * I, (e + 1) * I)).astype(np.float64).T
+        ref13[m] = dy13[m] @ sel(wt.w13t, np.arange(e * H, (e + 1) * H)).astype(np.float64).T
+    assert rel_frob(sel(b.dhact, rows), ref2) <= TOL
+    assert rel_frob(sel(b.dxperm, rows), ref13) <= TOL
+    # weight gradients (and their column operands) for a hot, an ordinary and an empty expert
+    rtok = host(rt.row_token).astype(np.int64)
+    for e in (hot, plain, empty):
+        a, z = int(po[e]), int(po[e + 1])
+        seg = np.arange(off[e], off[e + 1])
+        n = len(seg)
+        o2 = np.sort(r.choice(H, 24, replace=False))
+        o13 = np.sort(r.choice(2 * I, 24, replace=False))
+        got2, got13 = host(b.dw2[e])[o2], host(b.dw13[e])[o13]
+        if e == empty:
+            assert a == z and not got2.any() and not got13.any()
+            continue
+        hc = _dq_rows(f.hq, seg)            # [n, I]: the forward's NVFP4 SwiGLU output, dequantised
+        xc = _dq_rows(f.xq, rtok[seg])      # [n, H]: the forward's NVFP4 X rows in expert order
+        assert np.array_equal(host(b.hc[:, a:a + n]), hc.T) and not host(b.hc[:, a + n:z]).any()
+        assert np.array_equal(host(b.xc[:, a:a + n]), xc.T)
+        assert np.array_equal(host(b.dy2c[:, a:a + n]), d["dY2"][seg].T)
+        ref = d["dY2"][seg][:, o2].astype(np.float64).T @ hc.astype(np.float64)
+        assert rel_frob(got2, ref) <= TOL
+        ref = d["dY13"][seg][:, o13].astype(np.float64).T @ xc.astype(np.float64)
+        assert rel_frob(got13, ref) <= TOL
