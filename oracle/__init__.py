@@ -34,6 +34,7 @@ nvfp4     NVFP4 two-level block quantisation (rows and columns) and dequant.
 moe       routing, permutation, grouped GEMMs, SwiGLU and the weighted combine.
 pipeline  the whole expert-layer forward and backward with the GPU's storage
           roundings mirrored (for end-to-end reporting).
+philox    the Philox4x64-10 counter-based generator (stochastic rounding).
 
 Parity status: every function is pinned by tests under ``tests/`` against
 closed forms, invariants, brute force or exact rational arithmetic, except the
@@ -41,4 +42,4 @@ end-to-end ``pipeline`` functions, whose result after re-quantisation of
 intermediate tensors is *parity unpinned* (see ``pipeline``).
 """
 
-from . import formats, nvfp4, moe, pipeline  # noqa: F401
+from . import formats, philox, nvfp4, moe, pipeline  # noqa: F401

@@ -112,6 +112,28 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- E4M3
 
+def e2m1_encode_sr(v: np.ndarray, u24: np.ndarray) -> np.ndarray:
+    """Stochastic rounding onto the E2M1 grid (the pretraining recipe's gradient
+    rounding, *The 4-bitter Lesson*, section "Why is the NVFP4 pretraining recipe
+    not sufficient for RL?").  |v| >= 6 saturates to 6.  Otherwise, with lo and hi
+    the grid neighbours of |v|, the magnitude rounds up to hi exactly when
+    u24 * 2^-24 < (|v| - lo) / (hi - lo), so the probability of rounding up is that
+    fraction (to 24 bits) and the rounding is unbiased.  The sign comes from v.
+    Every quantity here is exact in FP64 (and in FP32: |v| - lo is exact because
+    lo = 0 or hi <= 2 lo, and the grid gaps are powers of two)."""
+    v = np.asarray(v, dtype=np.float32)
+    u24 = np.asarray(u24, dtype=np.uint32)
+    a = np.minimum(np.abs(v).astype(np.float64), E2M1_MAX)
+    i = np.searchsorted(E2M1_MAGNITUDES, a, side="right") - 1     # largest grid value <= a
+    lo = E2M1_MAGNITUDES[i]
+    top = i == len(E2M1_MAGNITUDES) - 1
+    gap = np.where(top, 1.0, E2M1_MAGNITUDES[np.minimum(i + 1, len(E2M1_MAGNITUDES) - 1)] - lo)
+    frac = (a - lo) / gap
+    up = (~top) & (u24.astype(np.float64) * 2.0 ** -24 < frac)
+    mag = (i + up).astype(np.uint8)
+    return (np.signbit(v).astype(np.uint8) << 3 | mag).astype(np.uint8)
+
+
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     """E4M3 byte -> FP64 value (closed form); 0x7F / 0xFF decode to NaN."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)

@@ -44,6 +44,13 @@ supports, used identically by the GPU path):
    BF16 (nearest, ties to even).  This is dequantisation in the quantiser's own
    precision followed by a cast to the BF16 storage format.
 
+8. Stochastic rounding (optional, the pretraining recipe's gradient rounding):
+   step 3's E2M1 rounding is replaced by ``formats.e2m1_encode_sr`` with one
+   24-bit uniform per element from ``philox`` (counter = (position >> 3,
+   output row, stream, 0), key = (seed, 0)); stream 0 for a row-direction output,
+   1 for a column-direction (transposed) output.  Block scales stay
+   round-to-nearest.
+
 Each FP32 step above is one correctly rounded operation (``formats.f32_div`` and
 ``formats.f32_mul``), so the integer results (codes, scale bytes) are exactly
 defined and the GPU path must reproduce them bit for bit.
@@ -56,6 +63,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import formats as F
+from . import philox
 
 BLOCK = 16
 SCALE_NUMERATOR = np.float32(6.0 * 448.0)   # largest E2M1 magnitude x largest E4M3 value
@@ -89,9 +97,12 @@ def tensor_scales(amax) -> tuple[np.ndarray, np.ndarray]:
     return S, G
 
 
-def quantize_blocks(x: np.ndarray, S_block: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quantize_blocks(x: np.ndarray, S_block: np.ndarray, sr_seed: int | None = None,
+                    sr_stream: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Readings 2 and 3 on x [rows, K] (FP32 values, K % 16 == 0) with the encode
-    scale given per block (S_block [rows, K/16]).  Returns (codes, scale bytes)."""
+    scale given per block (S_block [rows, K/16]); with sr_seed, reading 8 for the
+    elements (x is in its output layout: element (i, j) is position j of output
+    row i).  Returns (codes, scale bytes)."""
     x = np.asarray(x, dtype=np.float32)
     rows, K = x.shape
     if K % BLOCK:
@@ -107,7 +118,11 @@ def quantize_blocks(x: np.ndarray, S_block: np.ndarray) -> tuple[np.ndarray, np.
     safe = np.where(sf > 0, sf_val, np.float32(1))
     inv = np.where(sf > 0, F.f32_div(S_block, safe), np.float32(0)).astype(np.float32)
     v = F.f32_mul(xb, inv[:, :, None])
-    codes = F.e2m1_encode(v).reshape(rows, K)
+    if sr_seed is None:
+        codes = F.e2m1_encode(v).reshape(rows, K)
+    else:
+        u = philox.uniform24(np.arange(rows)[:, None], np.arange(K)[None, :], sr_stream, sr_seed)
+        codes = F.e2m1_encode_sr(v.reshape(rows, K), u)
     return codes, sf
 
 
@@ -138,8 +153,9 @@ def row_groups(rows: int, scale_mode: str, seg_offsets=None, nseg: int | None = 
 
 
 def quantize_rows(x: np.ndarray, scale_mode: str = "tensor", seg_offsets=None, nseg=None,
-                  amax=None) -> NVFP4:
-    """NVFP4 along the contiguous dimension K of x [rows, K]."""
+                  amax=None, sr_seed: int | None = None, _sr_stream: int = 0) -> NVFP4:
+    """NVFP4 along the contiguous dimension K of x [rows, K] (stochastic rounding of
+    the elements with sr_seed)."""
     x = np.asarray(x, dtype=np.float32)
     rows, K = x.shape
     grp, ngroups = row_groups(rows, scale_mode, seg_offsets, nseg)
@@ -149,7 +165,7 @@ def quantize_rows(x: np.ndarray, scale_mode: str = "tensor", seg_offsets=None, n
     amax = np.asarray(amax, dtype=np.float32).reshape(ngroups)
     S, G = tensor_scales(amax)
     S_block = np.repeat(S[grp][:, None], K // BLOCK, axis=1)
-    codes, sf = quantize_blocks(x, S_block)
+    codes, sf = quantize_blocks(x, S_block, sr_seed, _sr_stream)
     G_block = np.repeat(G[grp][:, None], K // BLOCK, axis=1)
     return NVFP4(codes, sf, G, G_block, amax)
 
@@ -161,7 +177,8 @@ def padded_offsets(seg_offsets) -> np.ndarray:
     return np.concatenate([[0], np.cumsum((n + BLOCK - 1) // BLOCK * BLOCK)]).astype(np.int64)
 
 
-def quantize_cols(x: np.ndarray, seg_offsets, scale_mode: str = "tensor", amax=None) -> tuple[NVFP4, np.ndarray]:
+def quantize_cols(x: np.ndarray, seg_offsets, scale_mode: str = "tensor", amax=None,
+                  sr_seed: int | None = None) -> tuple[NVFP4, np.ndarray]:
     """Reading 6, segmented-K form: x [R, C] -> NVFP4 of its transpose [C, Rpad],
     where the rows of segment s land in columns [po[s], po[s] + n_s) and the
     rest of the segment's padded range is zero.  The scale group is the whole
@@ -194,11 +211,12 @@ def quantize_cols(x: np.ndarray, seg_offsets, scale_mode: str = "tensor", amax=N
         G_block = np.broadcast_to(G[seg_of_block][None, :], (C, len(seg_of_block))).astype(np.float32)
     else:
         raise ValueError(scale_mode)
-    codes, sf = quantize_blocks(xt, S_block)
+    codes, sf = quantize_blocks(xt, S_block, sr_seed, 1)
     return NVFP4(codes, sf, G, G_block, amax), po
 
 
-def quantize_cols_batched(x: np.ndarray, nbatch: int, scale_mode: str = "segment", amax=None) -> NVFP4:
+def quantize_cols_batched(x: np.ndarray, nbatch: int, scale_mode: str = "segment", amax=None,
+                          sr_seed: int | None = None) -> NVFP4:
     """Reading 6, batched form (weights): x [nbatch*m, C] is nbatch matrices of
     m rows (m % 16 == 0); each is transposed to [C, m] and quantised along m.
     The result stacks the transposes: [nbatch*C, m].  Scale group: each matrix
@@ -210,8 +228,8 @@ def quantize_cols_batched(x: np.ndarray, nbatch: int, scale_mode: str = "segment
         raise ValueError("batched column quantisation needs equal matrices of 16k rows")
     xt = x.reshape(nbatch, m, C).transpose(0, 2, 1).reshape(nbatch * C, m)
     if scale_mode == "segment":
-        return quantize_rows(xt, "segment", nseg=nbatch, amax=amax)
-    return quantize_rows(xt, "tensor", amax=amax)
+        return quantize_rows(xt, "segment", nseg=nbatch, amax=amax, sr_seed=sr_seed, _sr_stream=1)
+    return quantize_rows(xt, "tensor", amax=amax, sr_seed=sr_seed, _sr_stream=1)
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
