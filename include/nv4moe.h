@@ -185,6 +185,29 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
+ * nvfp4_quantize_sr -- nvfp4_quantize with stochastic rounding of the elements
+ * (every argument as there, plus the seed).  [4BL] "Why is the NVFP4 pretraining
+ * recipe not sufficient for RL?": the pretraining recipe rounds gradients
+ * stochastically so that their quantisation is unbiased.
+ *
+ * The block scales are the round-to-nearest ones.  Each element v = fp32(x * inv)
+ * rounds |v| up to its upper E2M1 neighbour exactly when u < (|v| - lo) / (hi - lo)
+ * (|v| >= 6 saturates to 6), with u = (bits >> 8) * 2^-24 and bits a 32-bit word of
+ * Philox4x64-10 (Salmon et al., SC 2011): counter (pos >> 3, out_row, stream, 0),
+ * key (seed, 0), word (pos >> 1) & 3, its high half for odd pos.  pos and out_row
+ * are the element's position and row in its output tensor (for NV4_COLS the padded
+ * position, for NV4_COLS_BATCHED the stacked output row); stream is 0 for the
+ * NV4_ROWS output (and out_rows of NV4_ROWS_AND_COLS) and 1 for column outputs.
+ * Results depend only on the data, the seed and these positions: deterministic
+ * and independent of launch geometry.
+ */
+nv4_status nvfp4_quantize_sr(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                             const int32_t *row_index, int layout, int scale_mode, int nseg,
+                             const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                             const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
+                             void *ws, size_t ws_bytes, int32_t *dev_status, uint64_t seed, void *stream);
+
+/*
  * moe_permute -- route tokens to experts and permute them by expert.
  * [LBP] "What W4A4 GEMM Actually Changes" (expert routing concentrates
  * activations); [MTE] "Background: Same Weights Did Not Guarantee Same Policy"

@@ -6,6 +6,7 @@ current HIP stream, every step of the path runs in the library's HIP kernels.
 The entry points carry the names of the C ABI (include/nv4moe.h):
 
     nvfp4_quantize      NVFP4 quantisation (rows, columns, batched columns)
+    nvfp4_quantize_sr   the same with stochastic rounding of the elements
     moe_permute         top-k routing and stable permutation by expert (+ row gather)
     nvfp4_grouped_gemm  grouped NVFP4 x NVFP4 GEMM (GROUP_M with optional SwiGLU, GROUP_K)
     moe_combine         top-k weighted combine back to token order
@@ -65,6 +66,8 @@ _SIGS = {
     "nvfp4_quantize_workspace": (_SZ, [_I64, _I64, _I, _I, _I]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                             ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
+    "nvfp4_quantize_sr": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
+                               ctypes.POINTER(NV4Tensor), _P, _SZ, _P, ctypes.c_uint64, _P]),
     "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
     "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                          ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
@@ -147,11 +150,12 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
                    amax_in: torch.Tensor | None = None, amax_out: torch.Tensor | None = None,
                    out: NVFP4 | None = None, out_K: int | None = None, ws: torch.Tensor | None = None,
                    dev_status: torch.Tensor | None = None, row_index: torch.Tensor | None = None,
-                   out_rows: NVFP4 | None = None, stream=None) -> NVFP4:
+                   out_rows: NVFP4 | None = None, sr_seed: int | None = None, stream=None) -> NVFP4:
     """NVFP4-quantise a 2-D BF16/FP32 tensor (row stride x.stride(0)).  With row_index
     (int32 [rows]), logical row r is x row row_index[r] (rows = row_index.numel()).
     NV4_ROWS_AND_COLS returns the column output and fills `out_rows` (allocated when
-    None and then reachable as the result's `rows_out` attribute)."""
+    None and then reachable as the result's `rows_out` attribute).  With sr_seed the
+    elements round stochastically (nvfp4_quantize_sr)."""
     lib = load()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, K = x.shape
@@ -175,10 +179,14 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
                          device=x.device)
     d = out.c()
     d2 = out_rows.c() if out_rows is not None else None
-    _check(lib.nvfp4_quantize(_ptr(x), _dtype(x), rows, K, x.stride(0), _ptr(row_index), layout, scale_mode, nseg,
-                              _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(amax_in), _ptr(amax_out),
-                              ctypes.byref(d), None if d2 is None else ctypes.byref(d2), _ptr(ws),
-                              0 if ws is None else ws.numel(), _ptr(dev_status), _stream(stream)))
+    args = (_ptr(x), _dtype(x), rows, K, x.stride(0), _ptr(row_index), layout, scale_mode, nseg,
+            _ptr(seg_offsets), _ptr(seg_padded_offsets), _ptr(amax_in), _ptr(amax_out),
+            ctypes.byref(d), None if d2 is None else ctypes.byref(d2), _ptr(ws),
+            0 if ws is None else ws.numel(), _ptr(dev_status))
+    if sr_seed is None:
+        _check(lib.nvfp4_quantize(*args, _stream(stream)))
+    else:
+        _check(lib.nvfp4_quantize_sr(*args, ctypes.c_uint64(sr_seed & (2 ** 64 - 1)), _stream(stream)))
     out.scale_mode, out.nseg = d.scale_mode, d.nseg
     if d2 is not None:
         out_rows.scale_mode, out_rows.nseg = d2.scale_mode, d2.nseg
@@ -455,7 +463,7 @@ def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfl
 
 def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY2: torch.Tensor,
                  dY13: torch.Tensor, bufs: BackwardBuffers | None = None, stream=None,
-                 stage_events: list | None = None, dual: bool = True) -> BackwardBuffers:
+                 stage_events: list | None = None, dual: bool = True, sr_seed: int | None = None) -> BackwardBuffers:
     """The four backward grouped GEMMs of the expert layer, every operand re-quantised
     to NVFP4 along its new contraction dimension.
 
@@ -469,7 +477,9 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
     row and column quantisation (one amax per tensor): the row pass of dY records
     it, the forward recorded those of X and of the SwiGLU output.  With `dual`, each
     upstream gradient is read once for both its row and its column quantisation
-    (NV4_ROWS_AND_COLS); otherwise the two are separate passes."""
+    (NV4_ROWS_AND_COLS); otherwise the two are separate passes.  With sr_seed the
+    upstream gradients' elements round stochastically (the pretraining recipe's
+    gradient rounding): dY2 with seed sr_seed, dY13 with sr_seed + 1."""
     T, H = x.shape
     rt = fwd.routing
     E = rt.offsets.numel() - 1
@@ -480,25 +490,27 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
         bufs = alloc_backward(T, H, E, k, I, device=x.device)
     st = stream if stream is not None else torch.cuda.current_stream()
     seg = dict(layout=NV4_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets, stream=stream)
+    sr2 = None if sr_seed is None else sr_seed
+    sr13 = None if sr_seed is None else sr_seed + 1
     if dual:
         both = dict(layout=NV4_ROWS_AND_COLS, nseg=E, seg_offsets=rt.offsets, seg_padded_offsets=rt.padded_offsets,
                     stream=stream)
         with _Stage(stage_events, "quantize_dy2", st):
-            nvfp4_quantize(dY2, out=bufs.dy2c, out_rows=bufs.dy2q, amax_out=bufs.dy2_amax, **both)
+            nvfp4_quantize(dY2, out=bufs.dy2c, out_rows=bufs.dy2q, amax_out=bufs.dy2_amax, sr_seed=sr2, **both)
         with _Stage(stage_events, "quantize_dy13", st):
-            nvfp4_quantize(dY13, out=bufs.dy13c, out_rows=bufs.dy13q, amax_out=bufs.dy13_amax, **both)
+            nvfp4_quantize(dY13, out=bufs.dy13c, out_rows=bufs.dy13q, amax_out=bufs.dy13_amax, sr_seed=sr13, **both)
     else:
         with _Stage(stage_events, "quantize_dy2", st):
-            nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, stream=stream)
+            nvfp4_quantize(dY2, out=bufs.dy2q, amax_out=bufs.dy2_amax, sr_seed=sr2, stream=stream)
         with _Stage(stage_events, "quantize_dy13", st):
-            nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, stream=stream)
+            nvfp4_quantize(dY13, out=bufs.dy13q, amax_out=bufs.dy13_amax, sr_seed=sr13, stream=stream)
     with _Stage(stage_events, "dgrad_hact", st):
         nvfp4_grouped_gemm(bufs.dy2q, wt.w2t, rt.offsets, E, I, M_cap=R, C=bufs.dhact, stream=stream)
     with _Stage(stage_events, "dgrad_x", st):
         nvfp4_grouped_gemm(bufs.dy13q, wt.w13t, rt.offsets, E, H, M_cap=R, C=bufs.dxperm, stream=stream)
     if not dual:
         with _Stage(stage_events, "quantize_cols_dy2", st):
-            nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, **seg)
+            nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, sr_seed=sr2, **seg)
     with _Stage(stage_events, "quantize_cols_hact", st):
         nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
     with _Stage(stage_events, "wgrad_w2", st):
@@ -506,7 +518,7 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
                            stream=stream)
     if not dual:
         with _Stage(stage_events, "quantize_cols_dy13", st):
-            nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, **seg)
+            nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, sr_seed=sr13, **seg)
     with _Stage(stage_events, "quantize_cols_x", st):
         if fwd.token_scale:
             # the forward kept per-token amaxes: the tensor's comes from one quantisation

@@ -91,11 +91,14 @@ size_t nvfp4_quantize_workspace(int64_t rows, int64_t K, int layout, int scale_m
   return round256((size_t)std::max(ng, 1) * sizeof(float));
 }
 
-nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
-                          const int32_t *row_index, int layout, int scale_mode, int nseg,
-                          const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
-                          const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
-                          void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+// nvfp4_quantize and nvfp4_quantize_sr: the same validation and launch, the latter
+// with stochastic rounding of the elements
+static nv4_status quantize_impl(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                                const int32_t *row_index, int layout, int scale_mode, int nseg,
+                                const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                                const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
+                                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream, int sr,
+                                uint64_t sr_seed) {
   if (!out) return fail(NV4_EINVAL, "nvfp4_quantize: out descriptor is NULL");
   if (rows < 0 || K < 0) return fail(NV4_EINVAL, "nvfp4_quantize: negative shape");
   if (xtype != NV4_BF16 && xtype != NV4_F32) return fail(NV4_EINVAL, "nvfp4_quantize: bad input dtype");
@@ -194,7 +197,28 @@ nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t 
   a.out_K = (layout == NV4_COLS || both) ? out->K : o_K;
   a.dev_status = dev_status;
   a.ngroups = ng;
+  a.sr = sr;
+  a.sr_seed = sr_seed;
   return from_hip(nv4::launch_quantize(a, static_cast<hipStream_t>(stream)), "nvfp4_quantize");
+}
+
+nv4_status nvfp4_quantize(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                          const int32_t *row_index, int layout, int scale_mode, int nseg,
+                          const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                          const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
+                          void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  return quantize_impl(x, xtype, rows, K, ldx, row_index, layout, scale_mode, nseg, seg_offsets,
+                       seg_padded_offsets, amax_in, amax_out, out, out_rows, ws, ws_bytes, dev_status, stream, 0, 0);
+}
+
+nv4_status nvfp4_quantize_sr(const void *x, nv4_dtype xtype, int64_t rows, int64_t K, int64_t ldx,
+                             const int32_t *row_index, int layout, int scale_mode, int nseg,
+                             const int32_t *seg_offsets, const int32_t *seg_padded_offsets,
+                             const float *amax_in, float *amax_out, nv4_tensor *out, nv4_tensor *out_rows,
+                             void *ws, size_t ws_bytes, int32_t *dev_status, uint64_t seed, void *stream) {
+  return quantize_impl(x, xtype, rows, K, ldx, row_index, layout, scale_mode, nseg, seg_offsets,
+                       seg_padded_offsets, amax_in, amax_out, out, out_rows, ws, ws_bytes, dev_status, stream, 1,
+                       seed);
 }
 
 // ---------------------------------------------------------------- routing / permutation

@@ -29,6 +29,8 @@ struct QuantArgs {
   float *tscale2;
   int32_t *dev_status;
   int ngroups;
+  int sr;                             // 1: stochastic rounding of the elements
+  uint64_t sr_seed;
 };
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream);
 

@@ -15,6 +15,15 @@
 //
 // Memory: every kernel streams its input once with 16-byte loads (the amax pass
 // is a second read when the group amax is not supplied).
+//
+// Stochastic rounding (the pretraining recipe's gradient rounding, same section
+// "Why is the NVFP4 pretraining recipe not sufficient for RL?"), when asked for:
+// the E2M1 step rounds |v| up to its upper grid neighbour exactly when
+// u < (|v| - lo) / (hi - lo), u a 24-bit uniform per element from Philox4x64-10
+// (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with
+// counter (position >> 3, output row, stream, 0) and key (seed, 0); stream 0 for
+// row-direction outputs, 1 for column-direction outputs.  Block scales stay
+// round-to-nearest.
 #include <algorithm>
 #include <type_traits>
 
@@ -172,6 +181,60 @@ __device__ __forceinline__ float div6_rn(float m) {
   return q;
 }
 
+// Philox4x64-10: 10 rounds of two 64x64->128-bit products and a Feistel-like
+// mix, the key bumped by the Weyl constants after every round.
+struct Rand4 {
+  uint64_t w[4];
+};
+__device__ __forceinline__ Rand4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+  uint64_t k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
+    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += kW0;
+    k1 += kW1;
+  }
+  return Rand4{{c0, c1, c2, c3}};
+}
+
+// the 24-bit uniform of element j (0..7) of the 8-element run a Philox block covers
+__device__ __forceinline__ uint32_t uniform24(const Rand4 &r, int j) {
+  const uint64_t w = r.w[j >> 1];
+  return (uint32_t)((j & 1) ? (w >> 32) : (w & 0xFFFFFFFFull)) >> 8;
+}
+
+// E2M1 code of v by stochastic rounding with the uniform u24 * 2^-24: |v| saturates
+// at 6; between grid neighbours lo <= |v| < hi it rounds up iff u < (|v| - lo) / (hi -
+// lo).  |v| - lo is exact (lo = 0 or |v| <= 2 lo) and the gaps are powers of two, so
+// the comparison is exact.  The sign comes from v (-0 gives code 8).
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u24) {
+  const float a = fminf(fabsf(v), 6.0f);
+  const int i = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
+  const float lo = i < 4 ? 0.5f * (float)i : (i == 4 ? 2.0f : (i == 5 ? 3.0f : (i == 6 ? 4.0f : 6.0f)));
+  const float inv_gap = i < 4 ? 2.0f : (i < 6 ? 1.0f : 0.5f);
+  const float frac = __fmul_rn(a - lo, inv_gap);
+  const float u = (float)u24 * 0x1p-24f;
+  const uint32_t up = (i < 7 && u < frac) ? 1u : 0u;
+  return (__float_as_uint(v) >> 31 << 3) | (uint32_t)(i + up);
+}
+
+// 8 codes (one dword, element 2i in the low nibble of byte i) of the products
+// v[i] * inv by stochastic rounding, uniforms from one Philox block
+__device__ __forceinline__ uint32_t pack_e2m1_sr8(const float v[8], float inv, const Rand4 &r) {
+  uint32_t p = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p |= e2m1_sr(__fmul_rn(v[j], inv), uniform24(r, j)) << (4 * j);
+  return p;
+}
+
 // value of lane ^ 1 (quad permutation [1, 0, 3, 2] of the data-parallel primitives)
 __device__ __forceinline__ float xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -180,9 +243,11 @@ __device__ __forceinline__ float xor1(float v) {
 // Quantise one 8-element half-block held by this lane; the partner lane (lane ^ 1)
 // holds the other half of the same 16-element block.  With inv_tab, fp32(S / sf)
 // is read from a table of the 127 E4M3 values (the same correctly rounded
-// quotients).  Returns the packed codes and the block scale byte.
+// quotients).  Returns the packed codes and the block scale byte.  With SR the
+// codes round stochastically with the uniforms of Philox block `rnd`.
+template <bool SR = false>
 __device__ __forceinline__ uint32_t quant_half_block(const float v[8], float S, const float *inv_tab,
-                                                     uint32_t &sf_out, bool &bad) {
+                                                     uint32_t &sf_out, bool &bad, const Rand4 *rnd = nullptr) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -193,12 +258,13 @@ __device__ __forceinline__ uint32_t quant_half_block(const float v[8], float S, 
   m = fmaxf(m, xor1(m));
   const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
   const float inv = inv_tab ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
+  sf_out = sf;
+  if (SR) return pack_e2m1_sr8(v, inv, *rnd);
   uint32_t p = 0;
   p = pack_e2m1_pair<0>(p, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
   p = pack_e2m1_pair<1>(p, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
   p = pack_e2m1_pair<2>(p, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
   p = pack_e2m1_pair<3>(p, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
-  sf_out = sf;
   return p;
 }
 
@@ -220,7 +286,7 @@ __device__ void write_group_scales(const QuantArgs &a) {
 // the next two are in flight.  The two lanes of a block are always both active
 // or both inactive (K % 16 == 0 and runs start at multiples of 64 chunks).
 // With one tensor scale, fp32(S / sf) comes from an LDS table.
-template <bool F32, bool TENSOR>
+template <bool F32, bool TENSOR, bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
   __shared__ float inv_tab[128];
   if (blockIdx.x == 0) write_group_scales(a);
@@ -263,8 +329,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
       float v[8];
       unpack_chunk<F32>(cur[u], v);
       uint32_t sf, p;
+      Rand4 rnd;
+      if (SR) rnd = philox4x64_10((uint64_t)q[u].ch, (uint64_t)q[u].row, 0, 0, a.sr_seed);
       if (TENSOR) {
-        p = quant_half_block(v, S_tensor, inv_tab, sf, bad);
+        p = quant_half_block<SR>(v, S_tensor, inv_tab, sf, bad, &rnd);
       } else {
         const int64_t row = act ? q[u].row : 0;
         if (row < g_lo || row >= g_hi) {  // entered another group: its row range and scale
@@ -274,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
           else { g_lo = (int64_t)g * (a.rows / a.nseg); g_hi = g_lo + a.rows / a.nseg; }
           S = tensor_encode_scale(A[g]);
         }
-        p = quant_half_block(v, S, nullptr, sf, bad);
+        p = quant_half_block<SR>(v, S, nullptr, sf, bad, &rnd);
       }
       if (act) {
         codes[q[u].row * cstride + q[u].ch] = p;
@@ -289,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
 
 // Row layout with one scale per row (the per-token variant): one wave per row,
 // amax and quantisation fused (the row is read twice, the second time from cache).
-template <bool F32>
+template <bool F32, bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -321,7 +389,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
       float v[8];
       unpack_chunk<F32>(load_chunk<F32>(a.x, base + (act ? k : k0)), v);
       uint32_t sf;
-      const uint32_t p = quant_half_block(v, S, nullptr, sf, bad);
+      Rand4 rnd;
+      if (SR) rnd = philox4x64_10((uint64_t)(k >> 3), (uint64_t)row, 0, 0, a.sr_seed);
+      const uint32_t p = quant_half_block<SR>(v, S, nullptr, sf, bad, &rnd);
       if (act) {
         reinterpret_cast<uint32_t *>(a.codes)[row * (a.out_K >> 3) + (k >> 3)] = p;
         if (((k >> 3) & 1) == 0) a.scales[row * (a.out_K >> 4) + (k >> 4)] = (uint8_t)sf;
@@ -351,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
 constexpr int kOutPitch = 72;       // LDS out-tile row pitch for 64 code bytes (+8 breaks bank aliasing)
 constexpr int kScalePitch = 12;
 
-template <bool F32, int P, int C, bool ROWS_TOO>
+template <bool F32, int P, int C, bool ROWS_TOO, bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles_per_seg) {
   typedef typename std::conditional<F32, float, uint16_t>::type T;
   static_assert(P == 128, "tiles of 128 positions (8 blocks)");
@@ -444,7 +514,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   __syncthreads();
 
   bool bad = false;
-  auto quant16 = [&](const float v[16], float S, bool use_tab, uint32_t &lo, uint32_t &hi) -> uint32_t {
+  // rnd0 / rnd1: the Philox blocks of the 16 elements' positions (SR only)
+  auto quant16 = [&](const float v[16], float S, bool use_tab, uint32_t &lo, uint32_t &hi, const Rand4 &rnd0,
+                     const Rand4 &rnd1) -> uint32_t {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -454,6 +526,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     }
     const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
     const float inv = use_tab ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
+    if (SR) {
+      lo = pack_e2m1_sr8(v, inv, rnd0);
+      hi = pack_e2m1_sr8(v + 8, inv, rnd1);
+      return sf;
+    }
     lo = 0;
     hi = 0;
     lo = pack_e2m1_pair<0>(lo, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
@@ -482,7 +559,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
       for (int i = 0; i < 16; ++i) v[i] = tval(16 * j + i, c);
       const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[j]]);
       uint32_t lo, hi;
-      const uint32_t sf = quant16(v, S, uniform, lo, hi);
+      Rand4 r0, r1;
+      if (SR) {  // output row orow0 + c, positions p0 + 16 j + [0, 16), stream 1
+        const uint64_t pc = (uint64_t)((p0 >> 3) + 2 * j);
+        r0 = philox4x64_10(pc, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
+        r1 = philox4x64_10(pc + 1, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
+      }
+      const uint32_t sf = quant16(v, S, uniform, lo, hi, r0, r1);
       *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(lo, hi);
       oscales[c][j] = (uint8_t)sf;
     }
@@ -501,7 +584,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = tval(pp, run * 64 + b * 16 + i);
-        const uint32_t sf = quant16(v, S_tile, true, cw[2 * b], cw[2 * b + 1]);
+        Rand4 r0, r1;
+        if (SR) {  // row orow of the row-direction output, columns c0 + run*64 + b*16 + [0, 16), stream 0
+          const uint64_t pc = (uint64_t)((c0 + run * 64 + b * 16) >> 3);
+          r0 = philox4x64_10(pc, (uint64_t)orow, 0, 0, a.sr_seed);
+          r1 = philox4x64_10(pc + 1, (uint64_t)orow, 0, 0, a.sr_seed);
+        }
+        const uint32_t sf = quant16(v, S_tile, true, cw[2 * b], cw[2 * b + 1], r0, r1);
         sfw |= sf << (8 * b);
       }
       uint8_t *dst = a.codes2 + orow * (Ccols >> 1) + ((c0 + run * 64) >> 1);
@@ -531,9 +620,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
 
-}  // namespace
-
-hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
+template <bool SR>
+hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
   const int cus = device_cu_count();
   const int per_row = a.scale_mode == NV4_SCALE_ROW;
   const bool f32 = a.x_is_f32 != 0;
@@ -553,18 +641,18 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
   if (a.layout == NV4_ROWS) {
     if (per_row) {
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((a.rows + 3) / 4, (int64_t)cus * 16));
-      if (f32) k_quant_rows_per_row<true><<<grid, kThreads, 0, stream>>>(a);
-      else k_quant_rows_per_row<false><<<grid, kThreads, 0, stream>>>(a);
+      if (f32) k_quant_rows_per_row<true, SR><<<grid, kThreads, 0, stream>>>(a);
+      else k_quant_rows_per_row<false, SR><<<grid, kThreads, 0, stream>>>(a);
     } else {
       const int64_t chunks = a.rows * (a.K >> 3);
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + 2 * kThreads - 1) / (2 * kThreads), (int64_t)cus * 8));
       const bool tensor = a.scale_mode == NV4_SCALE_TENSOR;
       if (f32) {
-        if (tensor) k_quant_rows<true, true><<<grid, kThreads, 0, stream>>>(a);
-        else k_quant_rows<true, false><<<grid, kThreads, 0, stream>>>(a);
+        if (tensor) k_quant_rows<true, true, SR><<<grid, kThreads, 0, stream>>>(a);
+        else k_quant_rows<true, false, SR><<<grid, kThreads, 0, stream>>>(a);
       } else {
-        if (tensor) k_quant_rows<false, true><<<grid, kThreads, 0, stream>>>(a);
-        else k_quant_rows<false, false><<<grid, kThreads, 0, stream>>>(a);
+        if (tensor) k_quant_rows<false, true, SR><<<grid, kThreads, 0, stream>>>(a);
+        else k_quant_rows<false, false, SR><<<grid, kThreads, 0, stream>>>(a);
       }
     }
   } else {
@@ -586,14 +674,20 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
     const bool both = a.layout == NV4_ROWS_AND_COLS;
     dim3 grid(gx, gy);
     if (f32) {
-      if (both) k_quant_cols<true, P, 64, true><<<grid, kThreads, 0, stream>>>(a, ptiles);
-      else k_quant_cols<true, P, 64, false><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      if (both) k_quant_cols<true, P, 64, true, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      else k_quant_cols<true, P, 64, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
     } else {
-      if (both) k_quant_cols<false, P, 128, true><<<grid, kThreads, 0, stream>>>(a, ptiles);
-      else k_quant_cols<false, P, 128, false><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      if (both) k_quant_cols<false, P, 128, true, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      else k_quant_cols<false, P, 128, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
     }
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
+  return a.sr ? launch_quantize_t<true>(a, stream) : launch_quantize_t<false>(a, stream);
 }
 
 }  // namespace nv4

@@ -98,11 +98,11 @@ def tensor_scales(amax) -> tuple[np.ndarray, np.ndarray]:
 
 
 def quantize_blocks(x: np.ndarray, S_block: np.ndarray, sr_seed: int | None = None,
-                    sr_stream: int = 0) -> tuple[np.ndarray, np.ndarray]:
+                    sr_stream: int = 0, sr_rows=None, sr_pos0: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Readings 2 and 3 on x [rows, K] (FP32 values, K % 16 == 0) with the encode
     scale given per block (S_block [rows, K/16]); with sr_seed, reading 8 for the
-    elements (x is in its output layout: element (i, j) is position j of output
-    row i).  Returns (codes, scale bytes)."""
+    elements (x is in its output layout: element (i, j) is position sr_pos0 + j of
+    output row sr_rows[i], by default row i).  Returns (codes, scale bytes)."""
     x = np.asarray(x, dtype=np.float32)
     rows, K = x.shape
     if K % BLOCK:
@@ -121,7 +121,8 @@ def quantize_blocks(x: np.ndarray, S_block: np.ndarray, sr_seed: int | None = No
     if sr_seed is None:
         codes = F.e2m1_encode(v).reshape(rows, K)
     else:
-        u = philox.uniform24(np.arange(rows)[:, None], np.arange(K)[None, :], sr_stream, sr_seed)
+        ids = np.arange(rows) if sr_rows is None else np.asarray(sr_rows, np.int64)
+        u = philox.uniform24(ids[:, None], sr_pos0 + np.arange(K)[None, :], sr_stream, sr_seed)
         codes = F.e2m1_encode_sr(v.reshape(rows, K), u)
     return codes, sf
 
@@ -153,9 +154,10 @@ def row_groups(rows: int, scale_mode: str, seg_offsets=None, nseg: int | None = 
 
 
 def quantize_rows(x: np.ndarray, scale_mode: str = "tensor", seg_offsets=None, nseg=None,
-                  amax=None, sr_seed: int | None = None, _sr_stream: int = 0) -> NVFP4:
+                  amax=None, sr_seed: int | None = None, _sr_stream: int = 0, sr_rows=None) -> NVFP4:
     """NVFP4 along the contiguous dimension K of x [rows, K] (stochastic rounding of
-    the elements with sr_seed)."""
+    the elements with sr_seed; sr_rows: the rows' indices in the whole tensor when
+    x is a selection of its rows)."""
     x = np.asarray(x, dtype=np.float32)
     rows, K = x.shape
     grp, ngroups = row_groups(rows, scale_mode, seg_offsets, nseg)
@@ -165,7 +167,7 @@ def quantize_rows(x: np.ndarray, scale_mode: str = "tensor", seg_offsets=None, n
     amax = np.asarray(amax, dtype=np.float32).reshape(ngroups)
     S, G = tensor_scales(amax)
     S_block = np.repeat(S[grp][:, None], K // BLOCK, axis=1)
-    codes, sf = quantize_blocks(x, S_block, sr_seed, _sr_stream)
+    codes, sf = quantize_blocks(x, S_block, sr_seed, _sr_stream, sr_rows)
     G_block = np.repeat(G[grp][:, None], K // BLOCK, axis=1)
     return NVFP4(codes, sf, G, G_block, amax)
 
@@ -178,12 +180,14 @@ def padded_offsets(seg_offsets) -> np.ndarray:
 
 
 def quantize_cols(x: np.ndarray, seg_offsets, scale_mode: str = "tensor", amax=None,
-                  sr_seed: int | None = None) -> tuple[NVFP4, np.ndarray]:
+                  sr_seed: int | None = None, sr_rows=None, sr_pos0: int = 0) -> tuple[NVFP4, np.ndarray]:
     """Reading 6, segmented-K form: x [R, C] -> NVFP4 of its transpose [C, Rpad],
     where the rows of segment s land in columns [po[s], po[s] + n_s) and the
     rest of the segment's padded range is zero.  The scale group is the whole
     tensor (``tensor``) or each segment (``segment``).  Returns the tensor and
-    the padded offsets po."""
+    the padded offsets po.  For stochastic rounding of a selection of x's
+    columns and rows, sr_rows are the output rows (x's column indices) and sr_pos0
+    the position of the first row."""
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
     off = np.asarray(seg_offsets, dtype=np.int64)
@@ -211,7 +215,7 @@ def quantize_cols(x: np.ndarray, seg_offsets, scale_mode: str = "tensor", amax=N
         G_block = np.broadcast_to(G[seg_of_block][None, :], (C, len(seg_of_block))).astype(np.float32)
     else:
         raise ValueError(scale_mode)
-    codes, sf = quantize_blocks(xt, S_block, sr_seed, 1)
+    codes, sf = quantize_blocks(xt, S_block, sr_seed, 1, sr_rows, sr_pos0)
     return NVFP4(codes, sf, G, G_block, amax), po
 
 

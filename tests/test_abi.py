@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"nv4_version", "nv4_status_string", "nv4_last_error", "nvfp4_quantize_workspace",
                           "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
                           "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
-                          "nv4_to_bf16", "bf16_grouped_gemm"}
+                          "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr"}
 
 
 def test_binding_covers_every_symbol():
@@ -156,3 +156,12 @@ def test_bf16_gemm_validation(lib):
     assert g(mode=1, epi=0, ri=P, ldc=1536) == -3   # row index with GROUP_K
     assert g(ar=1 << 20, K=4096, ri=P) == -1     # A above 4 GiB
     assert g(E=0) == -1
+
+
+def test_quantize_sr_validates_like_quantize(lib):
+    d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 32, 64, 0, 1)
+    q = lambda K=64, ldx=64: lib.nvfp4_quantize_sr(ctypes.c_void_p(0x1000), 0, 32, K, ldx, None, 1, 0, 1, None, None,
+                                                   None, None, ctypes.byref(d), None, ctypes.c_void_p(0x1000), 1 << 20,
+                                                   None, ctypes.c_uint64(7), None)
+    assert q(K=40, ldx=40) == -2
+    assert q(ldx=32) == -1
