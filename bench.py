@@ -23,13 +23,13 @@ stream, the roofline of the dominant kernel, and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--config learner_64k]
-                    [--forward-only] [--token-scale] [--recipe nvfp4|dequantized|bf16-backward|bf16]
+                    [--forward-only] [--token-scale] [--recipe nvfp4|nvfp4-sr|dequantized|bf16-backward|bf16]
                     [--no-compare] [--no-cpu-baseline] [--no-graph]
 
 Besides the timed recipe (default: NVFP4 forward and backward), the same step is
 timed for the other recipes of the pages for comparison ("compare"): the BF16
-(unquantised) layer, and the NVFP4 forward with the dequantized or the BF16
-backward.
+(unquantised) layer, the NVFP4 forward with the dequantized or the BF16
+backward, and the NVFP4 backward with stochastically rounded gradients.
 """
 
 from __future__ import annotations
@@ -187,6 +187,8 @@ def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride
 RECIPES = {
     "nvfp4": "NVFP4 forward and NVFP4 backward (every backward operand re-quantised along its new "
              "contraction dimension)",
+    "nvfp4-sr": "NVFP4 forward and NVFP4 backward with the upstream gradients rounded stochastically "
+                "(Philox4x64-10, fixed seed)",
     "dequantized": "NVFP4 forward, dequantized backward (BF16 GEMMs on the BF16 values of the forward's "
                    "NVFP4 weights and activations, BF16 upstream gradients)",
     "bf16-backward": "NVFP4 forward, BF16 backward on the unquantised weights and activations",
@@ -194,10 +196,15 @@ RECIPES = {
 }
 DTYPES = {
     "nvfp4": "nvfp4 (e2m1 + e4m3 block scales, fp32 tensor scales) decoded exactly to f16, f16 MFMA, f32 accumulate",
+    "nvfp4-sr": "nvfp4 (stochastic rounding of the gradient elements) decoded exactly to f16, f16 MFMA, "
+                "f32 accumulate",
     "dequantized": "forward nvfp4 decoded exactly to f16 (f16 MFMA); backward bf16 MFMA; f32 accumulate",
     "bf16-backward": "forward nvfp4 decoded exactly to f16 (f16 MFMA); backward bf16 MFMA; f32 accumulate",
     "bf16": "bf16 MFMA, f32 accumulate",
 }
+
+
+SR_SEED = 0x5EED   # the stochastic-rounding seed of the timed steps (a training loop would vary it)
 
 
 def time_recipe(nv4, torch, np, cfg, inp, recipe, backward, args, stages: bool) -> dict:
@@ -212,7 +219,7 @@ def time_recipe(nv4, torch, np, cfg, inp, recipe, backward, args, stages: bool) 
         w = nv4.quantize_expert_weights(W13, W2) if nvfp4_fwd else None
         wt = None
         if backward:
-            if recipe == "nvfp4":
+            if recipe in ("nvfp4", "nvfp4-sr"):
                 wt = nv4.quantize_expert_weights_t(W13, W2)
             elif recipe == "dequantized":
                 wt = nv4.dequantize_expert_weights_t(w)
@@ -235,7 +242,7 @@ def time_recipe(nv4, torch, np, cfg, inp, recipe, backward, args, stages: bool) 
         fb = nv4.alloc_forward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
     bb = None
     if backward:
-        bb = (nv4.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I) if recipe == "nvfp4"
+        bb = (nv4.alloc_backward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I) if recipe in ("nvfp4", "nvfp4-sr")
               else nv4.alloc_backward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I))
 
     def step(ev=None):
@@ -247,6 +254,8 @@ def time_recipe(nv4, torch, np, cfg, inp, recipe, backward, args, stages: bool) 
             return
         if recipe == "nvfp4":
             nv4.moe_backward(x, fb, wt, dY2, dY13, bb, stage_events=ev)
+        elif recipe == "nvfp4-sr":
+            nv4.moe_backward(x, fb, wt, dY2, dY13, bb, stage_events=ev, sr_seed=SR_SEED)
         elif recipe == "dequantized":
             nv4.moe_backward_bf16(fb.xq, fb.hq, wt, dY2, dY13, fb.routing, bb, stage_events=ev)
         else:
@@ -364,7 +373,7 @@ def main():
     ms_step, stage_avg, counts = res["ms_per_step"], res["stages"], res["counts"]
     compare = {}
     if not args.no_compare:
-        others = ["bf16"] + (["dequantized", "bf16-backward"] if backward else [])
+        others = ["bf16"] + (["dequantized", "bf16-backward", "nvfp4-sr"] if backward else [])
         for rcp in others:
             if rcp == args.recipe:
                 continue
@@ -392,7 +401,8 @@ def main():
             gbs = b / (stage_avg[n] * 1e-3) / 1e9
             other[n] = {"achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "ms": round(stage_avg[n], 4)}
-    bf16_stage = args.recipe == "bf16" or (args.recipe != "nvfp4" and dom not in ("gemm1_swiglu", "gemm2"))
+    bf16_stage = args.recipe == "bf16" or (args.recipe in ("dequantized", "bf16-backward")
+                                           and dom not in ("gemm1_swiglu", "gemm2"))
     kernel = gemm[dom][1].replace("k_gemm", "k_gemm (BF16 operands)") if bf16_stage else gemm[dom][1]
     rec = {
         "metric": METRIC,
@@ -424,7 +434,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": kernel, "stage": dom,
                      "achieved": round(gemm[dom][0], 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm[dom][0] / PEAK_F16_MFMA_TFLOPS, 4),
-                     "traffic": measured_traffic(dom, cfg.name) if args.recipe == "nvfp4" else None},
+                     "traffic": measured_traffic(dom, cfg.name) if args.recipe in ("nvfp4", "nvfp4-sr") else None},
         "other_kernels": other,
     }
     if compare:
