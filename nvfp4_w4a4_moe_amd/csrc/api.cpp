@@ -433,8 +433,10 @@ nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_ten
                        const int32_t *row_index, int layout, int nseg, const int32_t *seg_offsets,
                        const int32_t *seg_padded_offsets, void *out, int64_t out_rows, int64_t out_cols,
                        void *stream) {
-  if ((x == nullptr) == (q == nullptr)) return fail(NV4_EINVAL, "nv4_to_bf16: give exactly one of x and q");
-  if (!out) return fail(NV4_EINVAL, "nv4_to_bf16: NULL out");
+  // an empty source (rows == 0) may come with NULL pointers: nothing is read
+  if (x && q) return fail(NV4_EINVAL, "nv4_to_bf16: give exactly one of x and q");
+  if (!x && !q && rows != 0) return fail(NV4_EINVAL, "nv4_to_bf16: give exactly one of x and q");
+  if (!out && out_rows * out_cols != 0) return fail(NV4_EINVAL, "nv4_to_bf16: NULL out");
   if (rows < 0 || K <= 0) return fail(NV4_EINVAL, "nv4_to_bf16: bad shape");
   if (K % 16) return fail(NV4_EALIGN, "nv4_to_bf16: K must be a multiple of 16");
   if (!aligned(out, 16)) return fail(NV4_EALIGN, "nv4_to_bf16: out must be 16-byte aligned");
@@ -447,7 +449,7 @@ nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_ten
     a.x = static_cast<const uint16_t *>(x);
     a.ldx = ldx;
     a.src_rows = x_rows;
-  } else {
+  } else if (q) {
     if (!q->codes || !q->scales || !q->tscale) return fail(NV4_EINVAL, "nv4_to_bf16: NULL tensor buffer");
     if (q->K != K) return fail(NV4_EINVAL, "nv4_to_bf16: q->K != K");
     if (!aligned(q->codes, 8)) return fail(NV4_EALIGN, "nv4_to_bf16: codes must be 8-byte aligned");

@@ -279,6 +279,11 @@ __device__ void write_group_scales(const QuantArgs &a) {
   }
 }
 
+// No elements (rows == 0 or K == 0): only the groups' decode scales (and amax_out)
+// are written.  The quantisation kernels would otherwise read x at offset 0 for
+// their idle lanes, which an empty x does not have.
+__global__ void k_group_scales(QuantArgs a) { write_group_scales(a); }
+
 // Row layout, tensor or segment scales: every lane quantises 8 consecutive
 // elements per chunk (one 16-byte BF16 load, one 4-byte code store); waves
 // stride over the flat (row, chunk) order so that loads and stores are fully
@@ -625,6 +630,13 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
   const int cus = device_cu_count();
   const int per_row = a.scale_mode == NV4_SCALE_ROW;
   const bool f32 = a.x_is_f32 != 0;
+  if (a.rows == 0 || a.K == 0) {
+    if (a.ngroups > 0) {
+      if (!a.amax_in) k_fill_zero<<<(a.ngroups + 255) / 256, 256, 0, stream>>>(a.amax_acc, a.ngroups);
+      k_group_scales<<<1, kThreads, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+  }
   // group amax pass (tensor / segment scales without a supplied amax)
   if (!a.amax_in && !per_row) {
     k_fill_zero<<<(a.ngroups + 255) / 256, 256, 0, stream>>>(a.amax_acc, a.ngroups);

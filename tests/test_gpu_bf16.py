@@ -380,3 +380,30 @@ def test_learner_dequantized_backward_sampled(gpu_lib):
         assert rel_frob(got2, ref) <= TOL
         ref = d["dY13"][seg][:, o13].astype(np.float64).T @ xc.astype(np.float64)
         assert rel_frob(got13, ref) <= TOL
+
+
+def test_bf16_edge_cases_empty_inputs(gpu_lib):
+    """Empty inputs: no rows to convert, every expert empty (GROUP_M writes nothing,
+    GROUP_K writes zeros), and the dense single-expert case (E = 1)."""
+    K, N, E = 64, 96, 4
+    z = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    assert gpu_lib.nv4_to_bf16(z).shape == (0, K)
+    off = dev_i32(np.zeros(E + 1, np.int64))
+    cols = gpu_lib.nv4_to_bf16(z, layout=gpu_lib.NV4_COLS, nseg=E, seg_offsets=off, seg_padded_offsets=off)
+    assert cols.shape[0] == K
+    B = dev_bf16(_bf16_vals((E * N, K), 3))
+    C = torch.full((8, N), 7.0, device="cuda")
+    gpu_lib.bf16_grouped_gemm(dev_bf16(_bf16_vals((8, K), 4)), B, off, E, N, M_cap=8, C=C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)                 # rows past offsets[E] are not written
+    Ac = torch.zeros((N, 64), dtype=torch.bfloat16, device="cuda")
+    Bc = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    Cw = torch.full((E, N, 32), 7.0, device="cuda")
+    gpu_lib.bf16_grouped_gemm(Ac, Bc, off, E, N, group_mode=gpu_lib.NV4_GROUP_K, C=Cw)
+    torch.cuda.synchronize()
+    assert not Cw.any()                        # empty contraction ranges give zeros
+    # one expert: a dense GEMM
+    A = _bf16_vals((300, 256), 5)
+    Bd = _bf16_vals((160, 256), 6, 0.05)
+    Cd = gpu_lib.bf16_grouped_gemm(dev_bf16(A), dev_bf16(Bd), dev_i32(np.array([0, 300])), 1, 160)
+    assert rel_frob(host(Cd), A.astype(np.float64) @ Bd.astype(np.float64).T) <= TOL

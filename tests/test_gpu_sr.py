@@ -147,3 +147,19 @@ def test_learner_sr_gradients_sampled(gpu_lib):
     got = host(qc.codes.index_select(0, cidx))[:, po[e] // 2: po[e + 1] // 2]
     assert np.array_equal(got, refc.packed())
     assert np.array_equal(host(qc.scales.index_select(0, cidx))[:, po[e] // 16: po[e + 1] // 16], refc.scales)
+
+
+def test_sr_empty_and_degenerate(gpu_lib):
+    """No rows; an all-zero tensor (scale 0, codes 0 whatever the uniforms);
+    values on the E2M1 grid times a power-of-two scale round exactly."""
+    for seed in (None, SEED):                  # an empty input reads nothing and writes G = 1
+        q = gpu_lib.nvfp4_quantize(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), sr_seed=seed)
+        assert q.codes.shape == (0, 32) and host(q.tscale)[0] == 1.0
+    q = gpu_lib.nvfp4_quantize(torch.zeros((40, 64), dtype=torch.bfloat16, device="cuda"), sr_seed=SEED)
+    torch.cuda.synchronize()
+    assert not host(q.codes).any() and not host(q.scales).any()
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6, 6], np.float32)
+    x = np.tile(grid, (32, 4)) * np.float32(2.0 ** -3)
+    q = gpu_lib.nvfp4_quantize(dev_bf16(x), sr_seed=SEED)
+    ref = Q.quantize_rows(x)
+    _same(q, ref)                              # on-grid values: stochastic = nearest
