@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import nvfp4_w4a4_moe_amd as nv4
 import synth
 from oracle import moe
 from oracle import nvfp4 as Q
@@ -302,17 +303,14 @@ def _dq_rows(t, rows) -> np.ndarray:
     codes = Q.unpack_codes(host(t.codes.index_select(0, idx)))
     sc = host(t.scales.index_select(0, idx))
     G = host(t.tscale).astype(np.float32)
-    if t.scale_mode == gpu_scale_tensor:
+    if t.scale_mode == nv4.NV4_SCALE_TENSOR:
         g = np.full(len(rows), G[0], np.float32)
-    elif t.scale_mode == gpu_scale_segment:
+    elif t.scale_mode == nv4.NV4_SCALE_SEGMENT:
         g = G[rows // (t.rows // t.nseg)]
     else:
         g = G[rows]
     Gb = np.repeat(g[:, None], sc.shape[1], axis=1)
     return Q.dequantize_bf16(Q.NVFP4(codes, sc, G, Gb, np.zeros(1, np.float32)))
-
-
-gpu_scale_tensor, gpu_scale_segment = 0, 1   # NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT
 
 
 def test_learner_dequantized_backward_sampled(gpu_lib):
