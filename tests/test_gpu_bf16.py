@@ -405,3 +405,63 @@ def test_bf16_edge_cases_empty_inputs(gpu_lib):
     Bd = _bf16_vals((160, 256), 6, 0.05)
     Cd = gpu_lib.bf16_grouped_gemm(dev_bf16(A), dev_bf16(Bd), dev_i32(np.array([0, 300])), 1, 160)
     assert rel_frob(host(Cd), A.astype(np.float64) @ Bd.astype(np.float64).T) <= TOL
+
+
+def test_learner_bf16_layer_sampled(gpu_lib):
+    """The unquantised BF16 layer, forward and backward, on the learner batch in the
+    launch configuration the benchmark times: sampled rows of the SwiGLU output,
+    the expert outputs, the combined tokens and both data gradients, and sampled
+    output rows of both weight gradients of a hot and an ordinary expert, each
+    against the oracle's FP64 products of the GPU's own BF16 stage inputs."""
+    cfg = synth.CONFIGS["learner_64k"]
+    E, H, I, R, T, k = cfg.E, cfg.H, cfg.I, cfg.R, cfg.T, cfg.k
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2, X = d["W13"], d["W2"], d["X"]
+    dW13, dW2 = dev_bf16(W13), dev_bf16(W2)
+    f = gpu_lib.moe_forward_bf16(dev_bf16(X), dev_f32(d["logits"]), dW13, dW2, k)
+    wt = gpu_lib.bf16_expert_weights_t(dW13, dW2)
+    bufs = gpu_lib.alloc_backward_bf16(T, H, E, k, I, dgrad_dtype=torch.float32)
+    b = gpu_lib.moe_backward_bf16(dev_bf16(X), f.hact, wt, dev_bf16(d["dY2"]), dev_bf16(d["dY13"]), f.routing, bufs)
+    torch.cuda.synchronize()
+    rt = f.routing
+    off = host(rt.offsets).astype(np.int64)
+    po = host(rt.padded_offsets).astype(np.int64)
+    rtok = host(rt.row_token).astype(np.int64)
+    counts = np.diff(off)
+    r = synth.rng(41)
+    sel = lambda t, rows: host(t.index_select(0, torch.as_tensor(np.asarray(rows, np.int64), device=t.device)))
+    rows = np.sort(r.choice(R, 160, replace=False))
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    h_ref = np.zeros((len(rows), I))
+    y_ref = np.zeros((len(rows), H))
+    dh_ref = np.zeros((len(rows), I))
+    dx_ref = np.zeros((len(rows), H))
+    hact_rows = sel(f.hact, rows).astype(np.float64)
+    for e in np.unique(e_of):
+        m = e_of == e
+        c1 = X[rtok[rows[m]]].astype(np.float64) @ W13[e].astype(np.float64).T
+        h_ref[m] = moe.swiglu(c1)
+        y_ref[m] = hact_rows[m] @ W2[e].astype(np.float64).T
+        dh_ref[m] = d["dY2"][rows[m]].astype(np.float64) @ W2[e].astype(np.float64)
+        dx_ref[m] = d["dY13"][rows[m]].astype(np.float64) @ W13[e].astype(np.float64)
+    assert rel_frob(hact_rows, h_ref) <= 4e-3          # BF16 storage of the SwiGLU output (2^-9 relative)
+    assert rel_frob(sel(f.y, rows), y_ref) <= TOL
+    assert rel_frob(sel(b.dhact, rows), dh_ref) <= TOL
+    assert rel_frob(sel(b.dxperm, rows), dx_ref) <= TOL
+    toks = np.sort(r.choice(T, 64, replace=False))
+    tr = host(rt.token_row)[toks].astype(np.int64)
+    y_tok = np.stack([sel(f.y, tr[:, j]) for j in range(k)], axis=1)           # [t, k, H]
+    o_ref = np.einsum("tk,tkh->th", host(rt.topk_w)[toks].astype(np.float64), y_tok.astype(np.float64))
+    assert rel_frob(sel(f.out, toks), o_ref) <= 4e-3                           # BF16 output
+    hot = int(np.argmax(counts))
+    plain = int(np.flatnonzero((counts > 0) & (counts < counts.max()))[0])
+    for e in (hot, plain):
+        seg = np.arange(off[e], off[e + 1])
+        o2 = np.sort(r.choice(H, 16, replace=False))
+        o13 = np.sort(r.choice(2 * I, 16, replace=False))
+        he = sel(f.hact, seg).astype(np.float64)
+        ref = d["dY2"][seg][:, o2].astype(np.float64).T @ he
+        assert rel_frob(host(b.dw2[e])[o2], ref) <= TOL
+        ref = d["dY13"][seg][:, o13].astype(np.float64).T @ X[rtok[seg]].astype(np.float64)
+        assert rel_frob(host(b.dw13[e])[o13], ref) <= TOL
+        assert np.array_equal(host(b.hc[:, po[e]:po[e] + len(seg)]), he.T.astype(np.float32))
