@@ -186,14 +186,28 @@ __device__ __forceinline__ float div6_rn(float m) {
 struct Rand4 {
   uint64_t w[4];
 };
+// 128-bit product of x and the constant m from four 32x32+64->64-bit multiply-adds
+// (v_mad_u64_u32), each carrying the previous partial sum:
+//   t = x0 m0,  u = x0 m1 + t_hi,  w = x1 m0 + u_lo,  hi = x1 m1 + u_hi + w_hi,
+//   lo = t_lo | w_lo << 32   (x m = t_lo + w_lo 2^32 + (x1 m1 + u_hi + w_hi) 2^64)
+__device__ __forceinline__ void mulhilo64(uint64_t x, uint64_t m, uint64_t &hi, uint64_t &lo) {
+  const uint32_t x0 = (uint32_t)x, x1 = (uint32_t)(x >> 32);
+  const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+  const uint64_t t = (uint64_t)x0 * m0;
+  const uint64_t u = (uint64_t)x0 * m1 + (t >> 32);
+  const uint64_t w = (uint64_t)x1 * m0 + (uint32_t)u;
+  lo = (uint32_t)t | (w << 32);
+  hi = (uint64_t)x1 * m1 + ((u >> 32) + (w >> 32));
+}
 __device__ __forceinline__ Rand4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0) {
   constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
   constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
   uint64_t k1 = 0;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(kM0, c0), lo0 = kM0 * c0;
-    const uint64_t hi1 = __umul64hi(kM1, c2), lo1 = kM1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(c0, kM0, hi0, lo0);
+    mulhilo64(c2, kM1, hi1, lo1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -217,13 +231,17 @@ __device__ __forceinline__ uint32_t uniform24(const Rand4 &r, int j) {
 // the comparison is exact.  The sign comes from v (-0 gives code 8).
 __device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u24) {
   const float a = fminf(fabsf(v), 6.0f);
-  const int i = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
-  const float lo = i < 4 ? 0.5f * (float)i : (i == 4 ? 2.0f : (i == 5 ? 3.0f : (i == 6 ? 4.0f : 6.0f)));
-  const float inv_gap = i < 4 ? 2.0f : (i < 6 ? 1.0f : 0.5f);
+  const uint32_t i = (uint32_t)(a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) +
+                     (a >= 4.0f) + (a >= 6.0f);
+  // grid gap around a: 0.5 below 2, 1 below 4, 2 above; lo = a rounded down to it
+  // (exact: the scalings are by powers of two)
+  const float gap = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+  const float inv_gap = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+  const float lo = __builtin_floorf(a * inv_gap) * gap;
   const float frac = __fmul_rn(a - lo, inv_gap);
   const float u = (float)u24 * 0x1p-24f;
-  const uint32_t up = (i < 7 && u < frac) ? 1u : 0u;
-  return (__float_as_uint(v) >> 31 << 3) | (uint32_t)(i + up);
+  const uint32_t up = u < frac ? 1u : 0u;  // frac is 0 at the top of the grid (a = 6)
+  return (__float_as_uint(v) >> 31 << 3) | (i + up);
 }
 
 // 8 codes (one dword, element 2i in the low nibble of byte i) of the products
