@@ -290,7 +290,8 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
  * The source is either x (BF16 [x_rows][ldx], ldx >= K, ldx % 8 == 0, 16-byte
  * aligned) or q (an NVFP4 tensor [q->rows][K] with its tscale grouping: per
  * tensor, per equal segment of q->rows/q->nseg rows, or per row); exactly one is
- * non-NULL.  The BF16 value of an NVFP4 element is
+ * non-NULL (with rows == 0 both may be NULL: nothing is read, and out may be NULL
+ * when it has no elements).  The BF16 value of an NVFP4 element is
  *   bf16_rne(fp32(e2m1(q) * sf * G))
  * where e2m1(q) * sf is exact and the product with G is one FP32 rounding.
  *   rows, K          logical rows (after the gather) and columns; K % 16 == 0.
