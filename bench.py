@@ -379,7 +379,8 @@ def main():
                 continue
             print(f"[bench] comparison recipe {rcp}", file=sys.stderr, flush=True)
             r = time_recipe(nv4, torch, np, cfg, inputs, rcp, backward, args, stages=False)
-            compare[rcp] = {"recipe": RECIPES[rcp], "ms_per_step": round(r["ms_per_step"], 4),
+            label = RECIPES[rcp] if backward else RECIPES[rcp].split(" forward")[0] + " forward only"
+            compare[rcp] = {"recipe": label, "ms_per_step": round(r["ms_per_step"], 4),
                             "tokens_per_s": round(cfg.T / (r["ms_per_step"] * 1e-3), 1),
                             "weight_prep_ms": round(r["weight_ms"], 4),
                             "time_vs_this_recipe": round(r["ms_per_step"] / ms_step, 4)}
