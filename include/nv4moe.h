@@ -267,6 +267,13 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
  *   C [E][N][ldc] (ldc >= M) gets A_e . B_e^T; an empty range gives zeros.
  *   Tensor scales per tensor.
  *   offsets    device int32 [E+1].
+ * ws, ws_bytes   optional device workspace (nvfp4_grouped_gemm_workspace() bytes,
+ *              4-byte aligned; NULL or 0 is allowed).  With it, GROUP_K workgroups
+ *              take tiles from a counter in the workspace, the largest experts'
+ *              first, which balances skewed expert sizes; without it every
+ *              workgroup walks a fixed share of the tiles.  Every tile is computed
+ *              whole by one workgroup either way, so the output is bitwise the same.
+ *              Calls that share a workspace must not overlap.
  * K (A->K == B->K) must be a positive multiple of 64: the kernel stages K in
  * 128-wide slices and reads 64-element halves; GROUP_K ranges only need 16.
  * Errors: EINVAL, EALIGN (K not a positive multiple of 64, A->K != B->K),
@@ -338,13 +345,14 @@ nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_ten
  *   [offsets[e], offsets[e+1]) (16-aligned, e.g. padded offsets, the layout
  *   nv4_to_bf16 NV4_COLS writes); C [E][N][ldc] gets A_e . B_e^T, an empty range
  *   zeros.  N is taken from a_rows.
+ *   ws, ws_bytes   as for nvfp4_grouped_gemm (the GROUP_K tile schedule).
  * Errors: EINVAL, EALIGN (K not a positive multiple of 32, misaligned operands),
  * EUNSUPPORTED (SWIGLU or a row index with GROUP_K), EHIP.
  */
 nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int64_t b_rows_n, int64_t K,
                              const int32_t *offsets, int E, int64_t M_cap, int64_t N, const int32_t *a_rows,
                              int group_mode, int epilogue, void *C, nv4_dtype ctype, int64_t ldc,
-                             float *amax_out, void *stream);
+                             float *amax_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * moe_combine -- weighted sum of each token's k expert outputs, back in token

@@ -77,7 +77,8 @@ _SIGS = {
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I64, _I, _I64, _P, _I, _P]),
     "nv4_to_bf16": (_I, [_P, _I64, _I64, ctypes.POINTER(NV4Tensor), _I64, _I64, _P, _I, _I, _P, _P, _P, _I64, _I64,
                          _P]),
-    "bf16_grouped_gemm": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P, _P]),
+    "bf16_grouped_gemm": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P, _P, _SZ,
+                               _P]),
 }
 
 
@@ -243,12 +244,21 @@ def moe_permute(logits: torch.Tensor | None, E: int, k: int, T: int | None = Non
     return Routing(topk_ids, topk_w, offsets, padded, row_token, token_row)
 
 
+def _gemm_ws(ws, group_mode, device):
+    """The GROUP_K tile-schedule workspace: the caller's, else a new one."""
+    if group_mode != NV4_GROUP_K:
+        return None
+    return ws if ws is not None else torch.empty(256, dtype=torch.uint8, device=device)
+
+
 def nvfp4_grouped_gemm(A: NVFP4, B: NVFP4, offsets: torch.Tensor, E: int, N: int, M_cap: int | None = None,
                        a_rows: torch.Tensor | None = None, group_mode: int = NV4_GROUP_M,
                        epilogue: int = NV4_EPI_NONE, out_dtype=torch.float32, C: torch.Tensor | None = None,
-                       amax_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                       amax_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
     """GROUP_M: C [M_cap, N] = per-expert A_e . B_e^T (SwiGLU: N output columns from 2N
-    rows of B per expert).  GROUP_K: C [E, N=A.rows, M=B.rows] over per-expert K ranges."""
+    rows of B per expert).  GROUP_K: C [E, N=A.rows, M=B.rows] over per-expert K ranges,
+    tiles balanced through the workspace `ws` (allocated when not given)."""
     lib = load()
     if group_mode == NV4_GROUP_M:
         if M_cap is None:
@@ -263,9 +273,10 @@ def nvfp4_grouped_gemm(A: NVFP4, B: NVFP4, offsets: torch.Tensor, E: int, N: int
         ldc = C.stride(1)
         M_cap = 0
     a, b = A.c(), B.c()
+    ws = _gemm_ws(ws, group_mode, A.codes.device)
     _check(lib.nvfp4_grouped_gemm(ctypes.byref(a), ctypes.byref(b), _ptr(offsets), E, M_cap, N, _ptr(a_rows),
-                                  group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out), None, 0,
-                                  _stream(stream)))
+                                  group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
     return C
 
 
@@ -443,6 +454,7 @@ class BackwardBuffers:
     dw13: torch.Tensor      # [E, 2I, H]
     x_amax: torch.Tensor | None = None  # tensor amax of X when the forward scaled per token
     x_tq: NVFP4 | None = None            # (its by-product: X quantised with one tensor scale)
+    gemm_ws: torch.Tensor | None = None  # the weight-gradient GEMMs' tile-schedule workspace
 
 
 def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfloat16, wgrad_dtype=torch.float32,
@@ -458,7 +470,8 @@ def alloc_backward(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfl
         dy13c=NVFP4.empty(2 * I, kc, 1, device), xc=NVFP4.empty(H, kc, 1, device),
         dw2=torch.empty((E, H, I), dtype=wgrad_dtype, device=device),
         dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device),
-        x_amax=torch.zeros((1,), dtype=torch.float32, device=device))
+        x_amax=torch.zeros((1,), dtype=torch.float32, device=device),
+        gemm_ws=torch.empty(256, dtype=torch.uint8, device=device))
 
 
 def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY2: torch.Tensor,
@@ -515,7 +528,7 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
         nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
     with _Stage(stage_events, "wgrad_w2", st):
         nvfp4_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
-                           stream=stream)
+                           ws=bufs.gemm_ws, stream=stream)
     if not dual:
         with _Stage(stage_events, "quantize_cols_dy13", st):
             nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, sr_seed=sr13, **seg)
@@ -532,7 +545,7 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
             nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)
     with _Stage(stage_events, "wgrad_w13", st):
         nvfp4_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
-                           stream=stream)
+                           ws=bufs.gemm_ws, stream=stream)
     return bufs
 
 
@@ -578,7 +591,8 @@ def nv4_to_bf16(src, layout: int = NV4_ROWS, nseg: int = 1, seg_offsets: torch.T
 def bf16_grouped_gemm(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, E: int, N: int,
                       M_cap: int | None = None, a_rows: torch.Tensor | None = None, group_mode: int = NV4_GROUP_M,
                       epilogue: int = NV4_EPI_NONE, out_dtype=torch.float32, C: torch.Tensor | None = None,
-                      amax_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      amax_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
     """nvfp4_grouped_gemm on BF16 operands A [a_rows, K] and B [b_rows, K] (K contiguous)."""
     lib = load()
     for t in (A, B):
@@ -597,9 +611,10 @@ def bf16_grouped_gemm(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, E
             C = torch.empty((E, A.shape[0], B.shape[0]), dtype=out_dtype, device=A.device)
         ldc = C.stride(1)
         M_cap = 0
+    ws = _gemm_ws(ws, group_mode, A.device)
     _check(lib.bf16_grouped_gemm(_ptr(A), A.shape[0], _ptr(B), B.shape[0], K, _ptr(offsets), E, M_cap, N,
                                  _ptr(a_rows), group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out),
-                                 _stream(stream)))
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return C
 
 
@@ -683,6 +698,7 @@ class BF16BackwardBuffers:
     xc: torch.Tensor        # [H, Kcap]
     dw2: torch.Tensor       # [E, H, I]
     dw13: torch.Tensor      # [E, 2I, H]
+    gemm_ws: torch.Tensor | None = None  # the weight-gradient GEMMs' tile-schedule workspace
 
 
 def alloc_backward_bf16(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torch.bfloat16,
@@ -695,7 +711,8 @@ def alloc_backward_bf16(T: int, H: int, E: int, k: int, I: int, dgrad_dtype=torc
         dxperm=torch.empty((R, H), dtype=dgrad_dtype, device=device),
         dy2c=b(H), hc=b(I), dy13c=b(2 * I), xc=b(H),
         dw2=torch.empty((E, H, I), dtype=wgrad_dtype, device=device),
-        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device))
+        dw13=torch.empty((E, 2 * I, H), dtype=wgrad_dtype, device=device),
+        gemm_ws=torch.empty(256, dtype=torch.uint8, device=device))
 
 
 def moe_backward_bf16(x_op, hact_op, wt: BF16TransposedWeights, dY2: torch.Tensor, dY13: torch.Tensor,
@@ -728,11 +745,11 @@ def moe_backward_bf16(x_op, hact_op, wt: BF16TransposedWeights, dY2: torch.Tenso
         nv4_to_bf16(hact_op, out=bufs.hc, **seg)
     with _Stage(stage_events, "wgrad_w2", st):
         bf16_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
-                          stream=stream)
+                          ws=bufs.gemm_ws, stream=stream)
     with _Stage(stage_events, "cols_dy13_x", st):
         nv4_to_bf16(dY13, out=bufs.dy13c, **seg)
         nv4_to_bf16(x_op, out=bufs.xc, row_index=rt.row_token, **seg)
     with _Stage(stage_events, "wgrad_w13", st):
         bf16_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
-                          stream=stream)
+                          ws=bufs.gemm_ws, stream=stream)
     return bufs

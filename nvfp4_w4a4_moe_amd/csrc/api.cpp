@@ -290,8 +290,8 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
 // ---------------------------------------------------------------- grouped GEMM
 
 size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K) {
-  (void)group_mode; (void)E; (void)M_cap; (void)N; (void)K;
-  return 0;
+  (void)E; (void)M_cap; (void)N; (void)K;
+  return group_mode == NV4_GROUP_K ? 256 : 0;  // the dynamic tile schedule's counter
 }
 
 nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
@@ -299,7 +299,6 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
                               int group_mode, int epilogue,
                               void *C, nv4_dtype ctype, int64_t ldc, float *amax_out,
                               void *ws, size_t ws_bytes, void *stream) {
-  (void)ws; (void)ws_bytes;
   if (!A || !B || !offsets || !C) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: NULL argument");
   if (E <= 0 || E > 1024) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: E must be in [1, 1024]");
   if (group_mode != NV4_GROUP_M && group_mode != NV4_GROUP_K)
@@ -340,6 +339,10 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
   g.c_is_f32 = ctype == NV4_F32;
   g.ldc = ldc;
   g.amax_out = amax_out;
+  if (group_mode == NV4_GROUP_K && ws && ws_bytes >= 4) {
+    if (!aligned(ws, 4)) return fail(NV4_EALIGN, "nvfp4_grouped_gemm: workspace must be 4-byte aligned");
+    g.tile_counter = static_cast<int32_t *>(ws);
+  }
   if (group_mode == NV4_GROUP_M) {
     const int64_t Nb = epilogue == NV4_EPI_SWIGLU ? 2 * N : N;
     if (N <= 0) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: N must be positive");
@@ -372,7 +375,7 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
 nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int64_t b_rows_n, int64_t K,
                              const int32_t *offsets, int E, int64_t M_cap, int64_t N, const int32_t *a_rows,
                              int group_mode, int epilogue, void *C, nv4_dtype ctype, int64_t ldc,
-                             float *amax_out, void *stream) {
+                             float *amax_out, void *ws, size_t ws_bytes, void *stream) {
   if (!A || !B || !offsets || !C) return fail(NV4_EINVAL, "bf16_grouped_gemm: NULL argument");
   if (E <= 0 || E > 1024) return fail(NV4_EINVAL, "bf16_grouped_gemm: E must be in [1, 1024]");
   if (group_mode != NV4_GROUP_M && group_mode != NV4_GROUP_K)
@@ -388,6 +391,10 @@ nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int
     return fail(NV4_EINVAL, "bf16_grouped_gemm: each operand must stay below 4 GiB");
   nv4::GemmArgs g{};
   g.operands_bf16 = 1;
+  if (group_mode == NV4_GROUP_K && ws && ws_bytes >= 4) {
+    if (!aligned(ws, 4)) return fail(NV4_EALIGN, "bf16_grouped_gemm: workspace must be 4-byte aligned");
+    g.tile_counter = static_cast<int32_t *>(ws);
+  }
   g.a_codes = static_cast<const uint8_t *>(A);
   g.a_scale_mode = NV4_SCALE_TENSOR;
   g.a_rows = a_rows_n;

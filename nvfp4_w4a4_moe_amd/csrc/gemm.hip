@@ -270,6 +270,22 @@ void k_gemm(GemmArgs g) {
     const int tm = (int)((g.b_rows + BN - 1) / BN);
     ntn = tm;
     total = (int64_t)E * tn * tm;
+    if (g.tile_counter) {
+      // Dynamic schedule: a tile's work grows with its expert's rows, so workgroups
+      // take tiles from a counter, largest experts first (tstart holds the experts in
+      // decreasing row count, ties by id).  Every tile is still computed whole by
+      // one workgroup, so the result does not depend on which one.
+      for (int e = tid; e < E; e += NT) {
+        const int n = g.offsets[e + 1] - g.offsets[e];
+        int rank = 0;
+        for (int f = 0; f < E; ++f) {
+          const int m = g.offsets[f + 1] - g.offsets[f];
+          rank += (m > n) || (m == n && f < e);
+        }
+        tstart[rank] = e;
+      }
+      __syncthreads();
+    }
   }
   const int G = gridDim.x;
   const int per_xcd = G / kXcds;
@@ -278,9 +294,22 @@ void k_gemm(GemmArgs g) {
   const float a_ts = (!A_ROW_SCALE && !Cfg::kBf16) ? g.a_tscale[0] : 1.0f;
   float amax_run = 0.0f;
 
+  // Dynamic schedule: thread 0 takes the first tile here and, during every tile,
+  // the next one; the index travels through an LDS slot that alternates with the
+  // iteration (written before the barrier that ends the K loop, read after it, never
+  // rewritten while a wave may still read it).
+  const bool dyn = GROUP == NV4_GROUP_K && g.tile_counter != nullptr;
+  if (dyn) {
+    if (tid == 0) scratch[0] = atomicAdd(g.tile_counter, 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot is written
+    block_barrier();
+  }
   for (int64_t it = 0;; ++it) {
-    const int64_t L = it * G + (int64_t)xcd * per_xcd + slot;
+    const int64_t L = dyn ? (int64_t)__builtin_amdgcn_readfirstlane(scratch[it & 1])
+                          : it * G + (int64_t)xcd * per_xcd + slot;
     if (L >= total) break;
+    int next_tile = 0;
+    if (dyn && tid == 0) next_tile = atomicAdd(g.tile_counter, 1);
     TileJob job;
     int64_t nt_idx;
     if (GROUP == NV4_GROUP_M) {
@@ -302,8 +331,9 @@ void k_gemm(GemmArgs g) {
       job.gather = false;
       const int tn = (int)((g.a_rows + BM - 1) / BM);
       const int64_t per_e = (int64_t)tn * ntn;
-      job.e = (int)(L / per_e);
-      const int64_t r = L - job.e * per_e;
+      const int rank = (int)(L / per_e);
+      job.e = g.tile_counter ? tstart[rank] : rank;
+      const int64_t r = L - (int64_t)rank * per_e;
       const int64_t tni = r / ntn;
       nt_idx = r - tni * ntn;
       job.m0 = tni * BM;
@@ -530,6 +560,7 @@ void k_gemm(GemmArgs g) {
       }
     }
     // every LDS read of this tile has been consumed; the next tile refills the ring
+    if (dyn && tid == 0) scratch[(it + 1) & 1] = next_tile;
     __builtin_amdgcn_s_waitcnt(0xC07F);
     block_barrier();
 
@@ -634,8 +665,16 @@ using GemmTileK = TileCfg<2, 2, 4, 2, 2, 2>;
 // of four 128 x 128 or eight 128 x 64 wave tiles.)
 using GemmTileBf16 = TileCfg<2, 2, 2, 4, 2, 2, true>;
 
+// clears the dynamic schedule's tile counter before a launch (a kernel, so that the
+// step can be captured into a graph)
+__global__ void k_zero_counter(int32_t *p) {
+  const int i = threadIdx.x;
+  if (i == 0) p[i] = 0;
+}
+
 template <int GROUP, int EPI, bool OUT_F32, bool ROWS, class Cfg = GemmTile>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
+  if (GROUP == NV4_GROUP_K && g.tile_counter) k_zero_counter<<<1, 64, 0, stream>>>(g.tile_counter);
   const int cus = device_cu_count();
   // resident workgroups per CU: two for NVFP4 (LDS and registers allow two), one for BF16
   int grid = cus * Cfg::kWavesPerSimd * 4 / (Cfg::kThreads / 64);

@@ -73,6 +73,7 @@ struct GemmArgs {
   int64_t ldc;
   float *amax_out;
   int operands_bf16;             // 1: a_codes / b_codes hold BF16 elements (no scales)
+  int32_t *tile_counter;         // GROUP_K: workspace word for the dynamic tile schedule, or null
 };
 hipError_t launch_grouped_gemm(const GemmArgs &a, hipStream_t stream);
 

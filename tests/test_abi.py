@@ -146,7 +146,7 @@ def test_to_bf16_validation(lib):
 def test_bf16_gemm_validation(lib):
     P = ctypes.c_void_p(0x1000)
     g = lambda A=P, ar=256, B=P, br=8 * 1536, K=2048, E=8, Mc=256, N=768, ri=None, mode=0, epi=1, ldc=768: \
-        lib.bf16_grouped_gemm(A, ar, B, br, K, P, E, Mc, N, ri, mode, epi, P, 1, ldc, None, None)
+        lib.bf16_grouped_gemm(A, ar, B, br, K, P, E, Mc, N, ri, mode, epi, P, 1, ldc, None, None, 0, None)
     assert g(K=2040) == -2                       # K % 32
     assert g(A=ctypes.c_void_p(0x1008)) == -2    # A misaligned
     assert g(N=700) == -1                        # B rows != E * 2N
