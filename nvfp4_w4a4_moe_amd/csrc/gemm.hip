@@ -20,9 +20,10 @@
 //   -> LDS (packed, XOR-swizzled 16-byte chunks, double buffered)
 //   -> each wave reads its fragments (one 16-byte read per 64 K per fragment row)
 //   -> decode to FP16 in registers -> MFMA.
-// K permutation: inside each 64-wide K slice, lane half h of an MFMA operand
-// supplies elements h*32 + s*8 + [0, 8) in MFMA step s, for both A and B, so that
-// one 16-byte LDS read gives a lane all 32 codes it needs for the slice.  Any
+// K permutation: inside each 128-wide K stage, lane half h of an MFMA operand
+// supplies elements h*64 + sub*32 + s*8 + [0, 8) in MFMA step 4*sub + s, for both A
+// and B.  One 16-byte LDS read gives a lane the 32 codes of a slice `sub`, and one
+// 4-byte read the scale bytes of all four of its blocks in the stage.  Any
 // permutation of K applied to both operands leaves the dot product unchanged.
 //
 // BF16 operands (the unquantised layer and the BF16 / dequantized backward of
@@ -37,6 +38,7 @@
 // (hardware assigns workgroup i to XCD i % 8) take consecutive tiles, which share
 // the A rows (same M tile) and the expert's B matrix in that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "nv4_device.h"
 #include "nv4_internal.h"
@@ -424,37 +426,52 @@ void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // LDS stage layout: per 64-wide K slice ("sub"), every fragment row reads 32
-    // codes (one 16-byte LDS read) and two scale bytes; MFMA step t = sub*4 + s
-    // consumes dword s of those codes with the scale of block s/2.
+    // LDS stage layout: a row holds the stage's 128 codes in four XOR-swizzled
+    // 16-byte chunks and its 8 scale bytes.  Lane half h takes stage elements
+    // h*64 + [0, 64): slice `sub` is chunk 2h + sub (32 codes, one 16-byte read) and
+    // scale bytes 4h + 2 sub + {0, 1}; MFMA step t = sub*4 + s consumes dword s of
+    // the slice with the scale of block s/2.
     constexpr int kSubs = BF ? 1 : BK / 64, kSteps = BK / 16;  // (NVFP4 only)
+    static_assert(BF || kSubs == 2, "NVFP4 stages of 128 codes");
     uint4 ca[kSubs][FM], cb[kSubs][FN];
     f16x2 sa[kSubs][FM], sbv[kSubs][FN];
-    auto lds_read = [&](int sub, const uint8_t *base, int kt) {
-      const int64_t k0 = kb0 + (int64_t)kt * BK;
-      const bool full = k0 >= job.k_lo && k0 + BK <= job.k_hi;
-      const uint8_t *sbase = base + kScBase;
-      // scale-byte mask of this lane's two blocks (k0 + sub*64 + h*32 + {0, 16}):
-      // blocks outside [k_lo, k_hi) decode to zero
-      uint32_t smask = 0xFFFFu;
-      if (!full) {
-        const int64_t kb = k0 + sub * 64 + h * 32;
-        smask = ((kb >= job.k_lo && kb < job.k_hi) ? 0x00FFu : 0u) |
-                ((kb + 16 >= job.k_lo && kb + 16 < job.k_hi) ? 0xFF00u : 0u);
+    // per-lane byte offsets inside a stage: the lane's fragment row (l32 of the
+    // wave's first fragment), its chunk of each slice, its 4 scale bytes; fragment i
+    // adds the constant i*32 rows.  The swizzle of row r depends on r & 12 only,
+    // that is on l32.
+    const int rowA = wm * FM * 32 + l32, rowB = BM + wn * FN * 32 + l32;
+    const int ch0 = swz(2 * h, l32) * 16, ch1 = swz(2 * h + 1, l32) * 16;
+    const int offA = rowA * RB, offB = rowB * RB;
+    const int soffA = kScBase + rowA * SB + 4 * h, soffB = kScBase + rowB * SB + 4 * h;
+    auto lds_read = [&](const uint8_t *base, int kt, auto full_c) {
+      constexpr bool kFull = decltype(full_c)::value;
+      // scale-byte mask of this lane's four blocks (k0 + h*64 + b*16, b = 0..3) when
+      // the stage is partial: blocks outside [k_lo, k_hi) decode to zero
+      uint32_t smask = 0xFFFFFFFFu;
+      if (!kFull) {
+        const int64_t kb = kb0 + (int64_t)kt * BK + h * 64;
+        smask = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (kb + 16 * b >= job.k_lo && kb + 16 * b < job.k_hi) smask |= 0xFFu << (8 * b);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int row = wm * FM * 32 + i * 32 + l32;
-        ca[sub][i] = *reinterpret_cast<const uint4 *>(base + row * RB + swz(sub * 2 + h, row) * 16);
-        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + row * SB + sub * 4 + 2 * h);
-        sa[sub][i] = e4m3x2_to_f16(s2 & smask);
+        ca[0][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch0);
+        ca[1][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch1);
+        uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffA + i * 32 * SB);
+        if (!kFull) s4 &= smask;
+        sa[0][i] = e4m3x2_to_f16<false>(s4);
+        sa[1][i] = e4m3x2_to_f16<true>(s4);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int row = wn * FN * 32 + j * 32 + l32;
-        cb[sub][j] = *reinterpret_cast<const uint4 *>(base + BM * RB + row * RB + swz(sub * 2 + h, row) * 16);
-        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sbase + (BM + row) * SB + sub * 4 + 2 * h);
-        sbv[sub][j] = e4m3x2_to_f16(s2 & smask);
+        cb[0][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch0);
+        cb[1][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch1);
+        uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffB + j * 32 * SB);
+        if (!kFull) s4 &= smask;
+        sbv[0][j] = e4m3x2_to_f16<false>(s4);
+        sbv[1][j] = e4m3x2_to_f16<true>(s4);
       }
     };
     auto decode = [&](int t, f16x8 (&av)[FM], f16x8 (&bv)[FN]) {
@@ -542,8 +559,9 @@ void k_gemm(GemmArgs g) {
         if constexpr (BF) {
           bf16_stage(base, kt);
         } else {
-#pragma unroll
-          for (int sub = 0; sub < kSubs; ++sub) lds_read(sub, base, kt);
+          const int64_t k0 = kb0 + (int64_t)kt * BK;
+          if (k0 >= job.k_lo && k0 + BK <= job.k_hi) lds_read(base, kt, std::true_type{});
+          else lds_read(base, kt, std::false_type{});
 #pragma unroll
           for (int t = 0; t < kSteps; ++t) {
             f16x8 av[FM], bv[FN];

@@ -78,9 +78,11 @@ __device__ __forceinline__ f16x8 decode8_f16(uint32_t w, f16x2 s2) {
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Two E4M3 scale bytes (low 16 bits of `w`) -> two FP16 values (exact).
+// Two E4M3 scale bytes (the low 16 bits of `w`, or the high 16 bits with HI) -> two
+// FP16 values (exact).
+template <bool HI = false>
 __device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
 // ---------------------------------------------------------------- wave reductions
