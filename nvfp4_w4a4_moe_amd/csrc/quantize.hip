@@ -455,9 +455,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   constexpr int kPasses = P / kRowsPerPass;
   constexpr int kColGroups = kThreads / C;            // threads per column in phase 2
   constexpr int kBlkPerThread = NB / kColGroups;
+  // The column output tile reuses the input tile's LDS once every read of the input
+  // is done (the column results wait in registers), so that four workgroups fit on
+  // a CU and keep more loads in flight.
+  struct OutTile {
+    uint8_t codes[C][kOutPitch];
+    uint8_t scales[C][kScalePitch];
+  };
+  static_assert(sizeof(OutTile) <= sizeof(T) * P * C, "output tile fits in the input tile");
   __shared__ __attribute__((aligned(16))) T tile[P][C];
-  __shared__ __attribute__((aligned(16))) uint8_t ocodes[C][kOutPitch];
-  __shared__ uint8_t oscales[C][kScalePitch];
+  OutTile &otile = *reinterpret_cast<OutTile *>(&tile[0][0]);
+  auto &ocodes = otile.codes;
+  auto &oscales = otile.scales;
   __shared__ int64_t bsrc[NB];
   __shared__ int bnum[NB], bgrp[NB];
   __shared__ float inv_tab[128];
@@ -571,29 +580,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     return F32 ? (float)t : __uint_as_float((uint32_t)t << 16);
   };
 
-  // 2. column blocks: lane = column, kColGroups threads per column share its blocks
-  {
-    const int c = threadIdx.x % C, grp = threadIdx.x / C;
-#pragma unroll
-    for (int jj = 0; jj < kBlkPerThread; ++jj) {
-      const int j = grp * kBlkPerThread + jj;
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = tval(16 * j + i, c);
-      const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[j]]);
-      uint32_t lo, hi;
-      Rand4 r0, r1;
-      if (SR) {  // output row orow0 + c, positions p0 + 16 j + [0, 16), stream 1
-        const uint64_t pc = (uint64_t)((p0 >> 3) + 2 * j);
-        r0 = philox4x64_10(pc, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
-        r1 = philox4x64_10(pc + 1, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
-      }
-      const uint32_t sf = quant16(v, S, uniform, lo, hi, r0, r1);
-      *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(lo, hi);
-      oscales[c][j] = (uint8_t)sf;
-    }
-  }
-  // 2b. row blocks of the tile's valid rows (tensor scale): each thread one row and
+  // 2. row blocks of the tile's valid rows (tensor scale): each thread one row and
   // a run of 4 blocks of 16 columns (32 code bytes, 4 scale bytes)
   if (ROWS_TOO) {
     constexpr int kRunsPerRow = C / 64;
@@ -622,9 +609,43 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
       *reinterpret_cast<uint32_t *>(a.scales2 + orow * (Ccols >> 4) + ((c0 + run * 64) >> 4)) = sfw;
     }
   }
+  // 3. column blocks: lane = column, kColGroups threads per column share its blocks
+  // (results wait in registers until the input tile has been read in full)
+  uint32_t col_lo[kBlkPerThread], col_hi[kBlkPerThread], col_sf[kBlkPerThread];
+  {
+    const int c = threadIdx.x % C, grp = threadIdx.x / C;
+#pragma unroll
+    for (int jj = 0; jj < kBlkPerThread; ++jj) {
+      const int j = grp * kBlkPerThread + jj;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = tval(16 * j + i, c);
+      const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[j]]);
+      uint32_t lo, hi;
+      Rand4 r0, r1;
+      if (SR) {  // output row orow0 + c, positions p0 + 16 j + [0, 16), stream 1
+        const uint64_t pc = (uint64_t)((p0 >> 3) + 2 * j);
+        r0 = philox4x64_10(pc, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
+        r1 = philox4x64_10(pc + 1, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
+      }
+      col_sf[jj] = quant16(v, S, uniform, lo, hi, r0, r1);
+      col_lo[jj] = lo;
+      col_hi[jj] = hi;
+    }
+  }
   __syncthreads();
+  {  // every read of the input tile is done: its LDS becomes the output tile
+    const int c = threadIdx.x % C, grp = threadIdx.x / C;
+#pragma unroll
+    for (int jj = 0; jj < kBlkPerThread; ++jj) {
+      const int j = grp * kBlkPerThread + jj;
+      *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(col_lo[jj], col_hi[jj]);
+      oscales[c][j] = (uint8_t)col_sf[jj];
+    }
+    __syncthreads();
+  }
 
-  // 3. coalesced stores: 8 lanes per output row, one block (8 code bytes) each
+  // 4. coalesced stores: 8 lanes per output row, one block (8 code bytes) each
   {
     const int j = threadIdx.x & 7, rr = threadIdx.x >> 3;
     const bool blk_ok = p0 + 16 * j < plimit;
