@@ -568,13 +568,37 @@ void k_gemm(GemmArgs g) {
             decode(t, av, bv);
             mfmas(av, bv);
           }
+          // Instruction order of the stage: the first step's decode, then every MFMA
+          // followed by an even share of the later steps' decode, so that a wave
+          // decodes the next step while its own MFMAs run (the compiler otherwise
+          // groups each step's MFMAs after its whole decode).
+          constexpr int kMf = kSteps * FM * FN, kDec = (FM + FN) * 8;
+          constexpr int kPer = (kDec * (kSteps - 1) + kMf - 1) / kMf;
+          __builtin_amdgcn_sched_group_barrier(0x002, kDec, 0);  // VALU
+#pragma unroll
+          for (int i = 0; i < kMf; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);  // VALU
+          }
         }
       };
-      for (int kt = 0; kt < nk; kt += S) {
-        stage(0, kt);
-        if (kt + 1 < nk) stage(1, kt + 1);
-        if (S > 2 && kt + 2 < nk) stage(2 % S, kt + 2);
-        if (S > 3 && kt + 3 < nk) stage(3 % S, kt + 3);
+      if constexpr (S == 2) {
+        // pairs of stages with no branch between them, then the odd stage: with a
+        // conditional second stage the accumulators were copied between registers
+        // on every iteration
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+          stage(0, kt);
+          stage(1, kt + 1);
+        }
+        if (kt < nk) stage(0, kt);
+      } else {
+        for (int kt = 0; kt < nk; kt += S) {
+          stage(0, kt);
+          if (kt + 1 < nk) stage(1, kt + 1);
+          if (S > 2 && kt + 2 < nk) stage(2 % S, kt + 2);
+          if (S > 3 && kt + 3 < nk) stage(3 % S, kt + 3);
+        }
       }
     }
     // every LDS read of this tile has been consumed; the next tile refills the ring
