@@ -1,0 +1,11 @@
+// NVFP4 grouped GEMM instantiations: the gate/up GEMM with the SwiGLU epilogue, per-row (per-token) A scales.
+#include "gemm_kernel.h"
+
+namespace nv4 {
+
+hipError_t launch_gemm_m_swiglu_rows(const GemmArgs &g, hipStream_t stream) {
+  return g.c_is_f32 ? launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, true, true>(g, stream)
+                    : launch_tile<NV4_GROUP_M, NV4_EPI_SWIGLU, false, true>(g, stream);
+}
+
+}  // namespace nv4
