@@ -707,11 +707,16 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
       }
     }
   } else {
-    // tiles of 128 positions x 128 (BF16) or 64 (FP32) columns; NV4_COLS: an upper
+    // tiles of 128 positions x 64 columns, or 128 columns for BF16 rows and columns
+    // together (the row blocks need 64 columns per thread); NV4_COLS: an upper
     // bound of the padded positions (rows + 15 per segment), tiles past the actual
-    // end exit at once
+    // end exit at once.  (Measured on the learner batch: the gathered column
+    // quantisation of X takes 0.71 ms with 64 columns, 0.85 ms with 128, 0.92 ms
+    // with 32 and 1.26 ms with 256; rows and columns together are 20 % slower with
+    // 64 columns than with 128.)
     constexpr int P = 128;
-    const int C = f32 ? 64 : 128;
+    const bool both = a.layout == NV4_ROWS_AND_COLS;
+    const int C = (!f32 && both) ? 128 : 64;
     const unsigned gx = (unsigned)std::max<int64_t>(1, (a.K + C - 1) / C);
     int ptiles;
     unsigned gy;
@@ -722,14 +727,13 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
       ptiles = 0;
       gy = (unsigned)std::max<int64_t>(1, (a.rows + 15 * (int64_t)a.nseg + P - 1) / P);
     }
-    const bool both = a.layout == NV4_ROWS_AND_COLS;
     dim3 grid(gx, gy);
     if (f32) {
       if (both) k_quant_cols<true, P, 64, true, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
       else k_quant_cols<true, P, 64, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
     } else {
       if (both) k_quant_cols<false, P, 128, true, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
-      else k_quant_cols<false, P, 128, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
+      else k_quant_cols<false, P, 64, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles);
     }
   }
   return hipGetLastError();
