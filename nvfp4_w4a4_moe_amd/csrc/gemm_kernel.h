@@ -698,13 +698,13 @@ void k_gemm(GemmArgs g) {
 
 // NVFP4 tiles: every wave computes 128 x 64 with two waves per SIMD, so that one
 // wave's FP16 decode overlaps the other's MFMAs; double-buffered LDS stages.
-//   GROUP_M: 256 x 256 per workgroup, eight waves (one workgroup per CU): the
-//            larger tile halves the operand bytes each MFMA pulls through L2.
-//   GROUP_K: 256 x 128 per workgroup, four waves, two workgroups per CU.
+// Both group modes use 256 x 256 per workgroup, eight waves (one workgroup per
+// CU): the larger tile halves the operand bytes each MFMA pulls through L2.
 // (Measured on the learner batch against 128 x 256 with four waves: the GROUP_M
-// GEMMs 3-5 % faster, the weight gradients 2-4 %.)
+// GEMMs 3-5 % faster.  With the interleaved stage order, the weight gradients are
+// 5-19 % faster than with 256 x 128 tiles of four waves, two workgroups per CU.)
 using GemmTile = TileCfg<2, 4, 4, 2, 2, 2>;
-using GemmTileK = TileCfg<2, 2, 4, 2, 2, 2>;
+using GemmTileK = GemmTile;
 // BF16 operands: 128 x 256 workgroup tiles of four 64 x 128 wave tiles, two
 // workgroups per CU, double-buffered 24 KB stages.  (Measured on the learner
 // batch: 15-25 % faster than 256 x 256 tiles with one workgroup per CU, whether
