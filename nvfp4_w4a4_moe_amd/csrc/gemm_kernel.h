@@ -722,7 +722,8 @@ template <int GROUP, int EPI, bool OUT_F32, bool ROWS, class Cfg = GemmTile>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
   if (GROUP == NV4_GROUP_K && g.tile_counter) k_zero_counter<<<1, 64, 0, stream>>>(g.tile_counter);
   const int cus = device_cu_count();
-  // resident workgroups per CU: two for NVFP4 (LDS and registers allow two), one for BF16
+  // resident workgroups per CU: enough for kWavesPerSimd waves on every SIMD (one
+  // eight-wave NVFP4 workgroup, two four-wave BF16 workgroups)
   int grid = cus * Cfg::kWavesPerSimd * 4 / (Cfg::kThreads / 64);
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
