@@ -127,7 +127,7 @@ __device__ __forceinline__ void store_row_b32(void *base, uint32_t bytes, uint32
       __builtin_bit_cast(uint32_t, v),
       __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
                                         0x00020000),
-      voff, 0, 0);
+      voff, 0, 2);  // non-temporal: FP32 results are read by the next kernel, not here
 }
 __device__ __forceinline__ void store_row_b16(void *base, uint32_t bytes, uint32_t voff, uint16_t v) {
   __builtin_amdgcn_raw_buffer_store_b16(
