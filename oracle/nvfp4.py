@@ -51,6 +51,15 @@ supports, used identically by the GPU path):
    1 for a column-direction (transposed) output.  Block scales stay
    round-to-nearest.
 
+9. Weight scale groups.  The pages give weights one FP32 scale per tensor and
+   count three projection matrices per expert (*The 4-bitter Lesson*, section
+   "Why is the NVFP4 pretraining recipe not sufficient for RL?", "Baseline
+   recipe" paragraph and footnote 5).  Each projection of each expert (gate,
+   up, down) is therefore its own scale group.  Where gate and up are stored
+   stacked in one matrix, they are two equal row segments with a scale each;
+   in the transposed matrix (the data-gradient operand) they are the two halves
+   of the new K dimension.
+
 Each FP32 step above is one correctly rounded operation (``formats.f32_div`` and
 ``formats.f32_mul``), so the integer results (codes, scale bytes) are exactly
 defined and the GPU path must reproduce them bit for bit.
@@ -224,7 +233,12 @@ def quantize_cols_batched(x: np.ndarray, nbatch: int, scale_mode: str = "segment
     """Reading 6, batched form (weights): x [nbatch*m, C] is nbatch matrices of
     m rows (m % 16 == 0); each is transposed to [C, m] and quantised along m.
     The result stacks the transposes: [nbatch*C, m].  Scale group: each matrix
-    (``segment``) or the whole tensor (``tensor``)."""
+    (``segment``), the whole tensor (``tensor``), or each half of each matrix's
+    rows (``segment_halves``: reading 9, two projections stacked in one matrix,
+    e.g. an expert's gate and up weights; the first half of the transposed
+    matrix's new K then carries the first projection's scale and the second half
+    the second's, so no block mixes them).  ``amax`` (optional) holds one value
+    per group in that order."""
     x = np.asarray(x, dtype=np.float32)
     R, C = x.shape
     m = R // nbatch
@@ -233,7 +247,22 @@ def quantize_cols_batched(x: np.ndarray, nbatch: int, scale_mode: str = "segment
     xt = x.reshape(nbatch, m, C).transpose(0, 2, 1).reshape(nbatch * C, m)
     if scale_mode == "segment":
         return quantize_rows(xt, "segment", nseg=nbatch, amax=amax, sr_seed=sr_seed, _sr_stream=1)
-    return quantize_rows(xt, "tensor", amax=amax, sr_seed=sr_seed, _sr_stream=1)
+    if scale_mode == "tensor":
+        return quantize_rows(xt, "tensor", amax=amax, sr_seed=sr_seed, _sr_stream=1)
+    if scale_mode != "segment_halves":
+        raise ValueError(scale_mode)
+    half = m // 2
+    if m % 2 or half % BLOCK:
+        raise ValueError("halves of a matrix must be whole blocks of 16 rows")
+    # group 2s + h: rows [s*m + h*half, s*m + (h+1)*half) of x
+    if amax is None:
+        amax = np.abs(x).reshape(2 * nbatch, half * C).max(axis=1) if x.size else np.zeros(2 * nbatch)
+    amax = np.asarray(amax, np.float32).reshape(2 * nbatch)
+    S, G = tensor_scales(amax)
+    nblk = m // BLOCK
+    grp = 2 * np.repeat(np.arange(nbatch), C)[:, None] + (np.arange(nblk)[None, :] >= nblk // 2)
+    codes, sf = quantize_blocks(xt, S[grp], sr_seed, 1)
+    return NVFP4(codes, sf, G, G[grp], amax)
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:

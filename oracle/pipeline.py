@@ -25,12 +25,20 @@ dequantised values of the exact NVFP4 tensors of the forward ("dequantized
 backward", applied to weights and activations).  The upstream gradients stay
 BF16 in both.
 
+Weights carry one FP32 scale per expert and projection (reading 9 of ``nvfp4``):
+gate, up and down are separate scale groups, in the forward layout and in the
+transposed layout of the data gradients.
+
 Storage roundings of the GPU path are mirrored (SwiGLU output stored as BF16,
 expert outputs as FP32), so these functions give an end-to-end oracle result.
-Parity unpinned: after an intermediate tensor is re-quantised, an FP32-vs-FP64
-accumulation difference upstream can move an element across an FP4 rounding
-boundary, so GPU and oracle pipelines agree only statistically; the tests pin
-every stage separately instead, each fed the GPU's own stage inputs.
+Pins: the single-expert top-1 forward equals a dense W4A4 SwiGLU MLP, and every
+gradient of ``moe_backward`` is the adjoint of its forward GEMM on the backward's
+own dequantised operands (tests/test_oracle_moe.py, tests/test_oracle_backward.py).
+Parity unpinned: the end-to-end agreement of the GPU pipeline with this one.
+After an intermediate tensor is re-quantised, an FP32-vs-FP64 accumulation
+difference upstream can move an element across an FP4 rounding boundary, so the
+two pipelines agree only statistically; the GPU tests pin every stage separately
+instead, each fed the GPU's own stage inputs.
 """
 
 from __future__ import annotations
@@ -49,6 +57,27 @@ def gather_rows(t: Q.NVFP4, row_token: np.ndarray) -> Q.NVFP4:
     return Q.NVFP4(t.codes[rt], t.scales[rt], t.G, t.G_block[rt], t.amax)
 
 
+def quantize_expert_weights(W13: np.ndarray, W2: np.ndarray) -> tuple[Q.NVFP4, Q.NVFP4]:
+    """Reading 9 of ``nvfp4``: one FP32 scale per expert and projection.  W13
+    [E, 2I, H] holds gate_e then up_e: 2E row segments of I rows, group 2e the
+    gate and 2e + 1 the up projection of expert e; W2 [E, H, I]: E segments."""
+    E, I2, H = W13.shape
+    W13q = Q.quantize_rows(np.asarray(W13, np.float32).reshape(E * I2, H), "segment", nseg=2 * E)
+    W2q = Q.quantize_rows(np.asarray(W2, np.float32).reshape(E * H, I2 // 2), "segment", nseg=E)
+    return W13q, W2q
+
+
+def quantize_expert_weights_t(W13: np.ndarray, W2: np.ndarray) -> tuple[Q.NVFP4, Q.NVFP4]:
+    """The data gradients' weight operands, transposed per expert and re-quantised
+    along the new K, with the forward's scale groups (reading 9 of ``nvfp4``):
+    W2^T [E*I, H] one scale per expert; W13^T [E*H, 2I] one scale per expert for
+    K in [0, I) (gate) and one for [I, 2I) (up)."""
+    E, I2, H = W13.shape
+    W2t = Q.quantize_cols_batched(np.asarray(W2, np.float32).reshape(E * H, I2 // 2), E)
+    W13t = Q.quantize_cols_batched(np.asarray(W13, np.float32).reshape(E * I2, H), E, "segment_halves")
+    return W2t, W13t
+
+
 def moe_forward(X: np.ndarray, logits: np.ndarray, W13: np.ndarray, W2: np.ndarray, k: int,
                 renorm: bool = False, out_bf16: bool = False) -> dict:
     """X [T, H] (FP32 values of BF16 inputs), logits [T, E], W13 [E, 2I, H] with
@@ -61,8 +90,7 @@ def moe_forward(X: np.ndarray, logits: np.ndarray, W13: np.ndarray, W2: np.ndarr
     perm = moe.permute(ids, E)
     Xq = Q.quantize_rows(X, "tensor")
     Xg = gather_rows(Xq, perm["row_token"])
-    W13q = Q.quantize_rows(np.asarray(W13, np.float32).reshape(E * I2, H), "segment", nseg=E)
-    W2q = Q.quantize_rows(np.asarray(W2, np.float32).reshape(E * H, I), "segment", nseg=E)
+    W13q, W2q = quantize_expert_weights(W13, W2)
     C1 = moe.grouped_gemm_m(Xg.dequant(), W13q.dequant(), perm["offsets"], E, I2)
     Hact = moe.swiglu(C1)
     Hact_bf16 = F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32(Hact)))
@@ -159,8 +187,7 @@ def moe_backward(X: np.ndarray, Hact_bf16: np.ndarray, W13: np.ndarray, W2: np.n
     Xperm = X[np.asarray(perm["row_token"], np.int64)]
     dY2q = Q.quantize_rows(dY2, "tensor")
     dY13q = Q.quantize_rows(dY13, "tensor")
-    W2t = Q.quantize_cols_batched(np.asarray(W2, np.float32).reshape(E * H, I), E)      # [E*I, H]
-    W13t = Q.quantize_cols_batched(np.asarray(W13, np.float32).reshape(E * I2, H), E)   # [E*H, 2I]
+    W2t, W13t = quantize_expert_weights_t(W13, W2)      # [E*I, H], [E*H, 2I]
     dHact = moe.grouped_gemm_m(dY2q.dequant(), W2t.dequant(), off, E, I)
     dXperm = moe.grouped_gemm_m(dY13q.dequant(), W13t.dequant(), off, E, H)
     dY2c, po = Q.quantize_cols(dY2, off)          # [H, Rpad]

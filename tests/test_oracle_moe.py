@@ -237,12 +237,14 @@ def test_single_expert_top1_layer_is_dense_w4a4_mlp():
     T, H, I = 48, 64, 32
     X = synth.activations(T, H, 40)
     W13 = synth.weights((1, 2 * I, H), 41)
+    W13[0, I:] *= 30.0                     # up and gate with very different amax
     W2 = synth.weights((1, H, I), 42)
     lg = np.zeros((T, 1), np.float32)
     r = pipeline.moe_forward(X, lg, W13, W2, 1)
     assert (r["topk_w"] == 1.0).all() and (r["perm"]["row_token"] == np.arange(T)).all()
     xq = Q.quantize_rows(X).dequant()
-    w13 = Q.quantize_rows(W13[0]).dequant()
+    # gate and up are separate projections with a scale each (reading 9 of the quantiser)
+    w13 = np.vstack([Q.quantize_rows(W13[0, :I]).dequant(), Q.quantize_rows(W13[0, I:]).dequant()])
     w2 = Q.quantize_rows(W2[0]).dequant()
     c = xq @ w13.T
     h = c[:, :I] / (1 + np.exp(-c[:, :I])) * c[:, I:]

@@ -204,3 +204,65 @@ def test_pack_roundtrip():
     assert p.shape == (7, 32)
     assert (p[:, 0] == (c[:, 0] | (c[:, 1] << 4))).all()
     assert (Q.unpack_codes(p) == c).all()
+
+
+def test_column_quantisation_with_segment_scales():
+    """quantize_cols(scale_mode='segment'): every segment's columns equal the row
+    quantisation of that segment's own padded transpose under its own tensor scale,
+    composed from the per-tensor row quantiser (pinned above); an empty segment
+    gets S = 1 and writes nothing."""
+    x = synth.activations(70, 48, seed=35)
+    x[20:53] *= 40.0                                  # a segment with a much larger amax
+    off = np.array([0, 20, 20, 53, 70])
+    qc, po = Q.quantize_cols(x, off, "segment")
+    assert po.tolist() == [0, 32, 32, 80, 112]
+    assert qc.G[1] == 1.0
+    for s in (0, 2, 3):
+        n = off[s + 1] - off[s]
+        width = po[s + 1] - po[s]
+        xt = np.zeros((48, width), np.float32)
+        xt[:, :n] = x[off[s]:off[s + 1]].T
+        qr = Q.quantize_rows(xt, amax=np.abs(x[off[s]:off[s + 1]]).max())
+        assert (qc.codes[:, po[s]:po[s + 1]] == qr.codes).all()
+        assert (qc.scales[:, po[s] // 16:po[s + 1] // 16] == qr.scales).all()
+        assert qc.G[s] == qr.G[0] and (qc.G_block[:, po[s] // 16:po[s + 1] // 16] == qr.G[0]).all()
+    assert qc.G[2] != qc.G[0]
+
+
+def test_expert_weights_one_scale_per_projection():
+    """Reading 9: gate, up and down of every expert are separate scale groups.  The
+    stacked W13 [E, 2I, H] quantises exactly like its gate and up matrices quantised
+    as separate tensors, and W2 like each expert's down matrix; the transposed W13
+    of the data gradient holds the gate transpose in K [0, I) and the up transpose
+    in [I, 2I), each with its own projection's scale (composed from the pinned
+    per-tensor row quantiser)."""
+    from oracle import pipeline as P
+    E, I, H = 3, 32, 48
+    W13 = synth.weights((E, 2 * I, H), seed=36)
+    W13[:, I:] *= 100.0                               # up amax ~100x the gate's
+    W2 = synth.weights((E, H, I), seed=37)
+    w13, w2 = P.quantize_expert_weights(W13, W2)
+    w2t, w13t = P.quantize_expert_weights_t(W13, W2)
+    assert w13.G.shape == (2 * E,) and w2.G.shape == (E,) and w13t.G.shape == (2 * E,)
+    for e in range(E):
+        g = Q.quantize_rows(W13[e, :I])
+        u = Q.quantize_rows(W13[e, I:])
+        d = Q.quantize_rows(W2[e])
+        r = slice(2 * I * e, 2 * I * e + I)
+        assert (w13.codes[r] == g.codes).all() and (w13.scales[r] == g.scales).all() and w13.G[2 * e] == g.G[0]
+        r = slice(2 * I * e + I, 2 * I * (e + 1))
+        assert (w13.codes[r] == u.codes).all() and (w13.scales[r] == u.scales).all() and w13.G[2 * e + 1] == u.G[0]
+        assert (w2.codes[H * e:H * (e + 1)] == d.codes).all() and w2.G[e] == d.G[0]
+        assert w13.G[2 * e + 1] > 50 * w13.G[2 * e]
+        gt = Q.quantize_rows(W13[e, :I].T.copy())
+        ut = Q.quantize_rows(W13[e, I:].T.copy())
+        rows = slice(H * e, H * (e + 1))
+        assert (w13t.codes[rows, :I] == gt.codes).all() and (w13t.codes[rows, I:] == ut.codes).all()
+        assert (w13t.scales[rows, :I // 16] == gt.scales).all() and (w13t.scales[rows, I // 16:] == ut.scales).all()
+        assert w13t.G[2 * e] == gt.G[0] and w13t.G[2 * e + 1] == ut.G[0]
+        assert (w13t.G_block[rows, :I // 16] == gt.G[0]).all() and (w13t.G_block[rows, I // 16:] == ut.G[0]).all()
+        dt = Q.quantize_rows(W2[e].T.copy())
+        assert (w2t.codes[I * e:I * (e + 1)] == dt.codes).all() and w2t.G[e] == dt.G[0]
+        # the dequantised transposes equal the transposes of the forward's own values
+        # only up to requantisation; their scales are the forward groups' scales
+        assert w13t.G[2 * e] == w13.G[2 * e] and w13t.G[2 * e + 1] == w13.G[2 * e + 1]
