@@ -124,6 +124,7 @@ def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride
     from oracle import formats as F
     from oracle import moe
     from oracle import nvfp4 as Q
+    from oracle import pipeline
     try:
         import threadpoolctl
         cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
@@ -137,11 +138,14 @@ def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride
     off, rtok = perm["offsets"], perm["row_token"]
     experts = [e for e in range(0, E, expert_stride) if 0 < off[e + 1] - off[e] <= max_rows][:max_experts]
     amax_x = np.abs(X).max()
-    w13 = {e: Q.quantize_rows(d["W13"][e]).dequant() for e in experts}
-    w2 = {e: Q.quantize_rows(d["W2"][e]).dequant() for e in experts}
+    # one scale per expert and projection (gate, up, down), as the forward uses
+    wq = {e: pipeline.quantize_expert_weights(d["W13"][e:e + 1], d["W2"][e:e + 1]) for e in experts}
+    w13 = {e: wq[e][0].dequant() for e in experts}
+    w2 = {e: wq[e][1].dequant() for e in experts}
     if backward:
-        w2t = {e: Q.quantize_cols_batched(d["W2"][e], 1).dequant() for e in experts}     # [I, H]
-        w13t = {e: Q.quantize_cols_batched(d["W13"][e], 1).dequant() for e in experts}   # [H, 2I]
+        wtq = {e: pipeline.quantize_expert_weights_t(d["W13"][e:e + 1], d["W2"][e:e + 1]) for e in experts}
+        w2t = {e: wtq[e][0].dequant() for e in experts}     # [I, H]
+        w13t = {e: wtq[e][1].dequant() for e in experts}    # [H, 2I]
         amax_dy2, amax_dy13 = np.abs(d["dY2"]).max(), np.abs(d["dY13"]).max()
     Ts = min(token_sample, cfg.T)
     # per-token stages on the token sample
@@ -182,6 +186,65 @@ def cpu_baseline(d, cfg, backward: bool, token_sample: int = 4096, expert_stride
                        f"{'forward and backward' if backward else 'forward'} expert stages for {len(experts)} of {E} "
                        f"experts ({rows} of {cfg.R} routed rows, {t2 - t1:.2f} s, scaled by routed rows to "
                        f"{expert:.2f} s); FP64 numpy, BLAS threads {cores}")}
+
+
+def timed_events(torch, fn, reps: int, stream, flush=None) -> list:
+    """Milliseconds of `reps` calls of fn(), each bracketed by HIP events on `stream`
+    (the stream the kernels are launched on); with `flush`, a call of flush() before
+    every rep (outside the events) evicts the caches."""
+    out = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def stats(ms: list) -> dict:
+    import numpy as np
+    a = np.asarray(ms, np.float64)
+    return {"median_ms": round(float(np.median(a)), 5), "min_ms": round(float(a.min()), 5),
+            "max_ms": round(float(a.max()), 5), "reps": len(ms)}
+
+
+def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
+    """What plain kernels reach on this device (include/nv4moe_bench.h): a 16-byte
+    non-temporal stream copy of 1 GiB (2 GiB of traffic), a read-only stream of 2 GiB,
+    and a loop of FP16 32x32x16 MFMAs with one and two waves per SIMD.  Median, min and
+    max over `reps` event-timed calls; the rate is reported at the median."""
+    st = torch.cuda.current_stream()
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    big = torch.ones(2 * n // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for _ in range(3):
+        nv4.nv4_bench_copy(src, dst)
+        nv4.nv4_bench_read(big, sink)
+    c = stats(timed_events(torch, lambda: nv4.nv4_bench_copy(src, dst), reps, st))
+    c["gbs"] = round(2 * n / (c["median_ms"] * 1e-3) / 1e9, 1)
+    c["kernel"] = "k_stream_copy"
+    res["copy"] = c
+    r = stats(timed_events(torch, lambda: nv4.nv4_bench_read(big, sink), reps, st))
+    r["gbs"] = round(2 * n / (r["median_ms"] * 1e-3) / 1e9, 1)
+    r["kernel"] = "k_stream_read"
+    res["read"] = r
+    del src, dst, big
+    out = None
+    for w in (1, 2):
+        out, fl = nv4.nv4_bench_mfma(out, 4096, w)
+        m = stats(timed_events(torch, lambda: nv4.nv4_bench_mfma(out, 4096, w), max(5, reps // 4), st))
+        m["tflops"] = round(fl / (m["median_ms"] * 1e-3) / 1e12, 1)
+        m["kernel"] = f"k_mfma_loop<{w}>"
+        res[f"mfma_f16_{w}wave"] = m
+    torch.cuda.synchronize()
+    return res
 
 
 RECIPES = {
@@ -329,6 +392,8 @@ def main():
                     help="skip timing the other recipes (BF16 layer, dequantized and BF16 backward) for comparison")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every kernel from Python each step instead of replaying a captured HIP graph")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the device's achievable stream-copy, stream-read and FP16 MFMA rates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (three times): the known-size kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the GEMM's traffic counters")
@@ -355,6 +420,10 @@ def main():
     import synth
 
     nv4.load()
+    if args.ceilings:
+        print(json.dumps({"ceilings": measure_ceilings(nv4, torch), "peak_hbm_gbs": PEAK_HBM_GBS,
+                          "peak_f16_mfma_tflops": PEAK_F16_MFMA_TFLOPS}))
+        return
     cfg = synth.CONFIGS[args.config]
     backward = not args.forward_only
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)

@@ -81,6 +81,9 @@ typedef enum nv4_dtype { NV4_BF16 = 0, NV4_F32 = 1 } nv4_dtype;
 #define NV4_SCALE_TENSOR 0  /* one G for the whole tensor */
 #define NV4_SCALE_SEGMENT 1 /* one G per segment (expert) */
 #define NV4_SCALE_ROW 2     /* one G per row: the per-token variant */
+#define NV4_SCALE_SEGMENT_HALVES 3 /* one G per half of each segment's rows (NV4_COLS_BATCHED): two
+                                    * projections stacked in one matrix, e.g. an expert's gate and up
+                                    * weights; in the transposed output they are the two halves of K */
 
 /* grouped GEMM */
 #define NV4_GROUP_M 0       /* expert e owns rows [offsets[e], offsets[e+1]) of A and C */
@@ -103,7 +106,18 @@ typedef enum nv4_dtype { NV4_BF16 = 0, NV4_F32 = 1 } nv4_dtype;
  *   scales [rows][K/16]  E4M3 block scales, row-major
  *   tscale               FP32 decode scales G: 1 (SCALE_TENSOR), nseg
  *                        (SCALE_SEGMENT: segment s = rows [s*rows/nseg, (s+1)*rows/nseg)
- *                        when used as a grouped-GEMM B operand) or rows (SCALE_ROW)
+ *                        when used as a grouped-GEMM B operand), rows (SCALE_ROW), or
+ *                        2*nseg (SCALE_SEGMENT_HALVES: segment s = rows [s*rows/nseg,
+ *                        (s+1)*rows/nseg), tscale[2s] for columns [0, K/2) and
+ *                        tscale[2s+1] for [K/2, K))
+ *
+ * Weight scale groups ([4BL] "Why is the NVFP4 pretraining recipe not sufficient for
+ * RL?": one FP32 scale per weight tensor; its footnote 5 counts three projection
+ * matrices per expert): every projection of every expert has its own G.  The
+ * stacked gate/up weights W13 [E*2I][K] are SCALE_SEGMENT with nseg = 2E (segment 2e
+ * is gate_e, 2e+1 is up_e); the down weights W2 [E*H][I] SCALE_SEGMENT with nseg = E;
+ * the per-expert transposes of the data gradients are NV4_COLS_BATCHED outputs: W2^T
+ * SCALE_SEGMENT (nseg = E) and W13^T [E*H][2I] SCALE_SEGMENT_HALVES (nseg = E).
  */
 typedef struct nv4_tensor {
   uint8_t *codes;
@@ -157,7 +171,11 @@ const char *nv4_last_error(void);
  *                    NV4_SCALE_SEGMENT (one G per segment; ROWS/COLS_BATCHED use
  *                    equal segments of rows/nseg rows when seg_offsets is NULL),
  *                    NV4_SCALE_ROW (ROWS layout only: one G per row, computed in
- *                    the same single pass).  ngroups = 1, nseg or rows.
+ *                    the same single pass), NV4_SCALE_SEGMENT_HALVES
+ *                    (NV4_COLS_BATCHED only, rows/nseg % 32 == 0: group 2s is the
+ *                    first half of matrix s's rows, 2s+1 the second half; the output
+ *                    row of the transpose then has K/2-column halves with a G each).
+ *                    ngroups = 1, nseg, rows or 2*nseg.
  *   seg_offsets      device int32 [nseg+1], non-decreasing, seg_offsets[nseg] == rows;
  *                    required for NV4_COLS, optional for SCALE_SEGMENT with ROWS.
  *   seg_padded_offsets device int32 [nseg+1], required for NV4_COLS: the 16-padded
@@ -252,9 +270,15 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
  *              A->tscale per tensor or per row.  With a_rows != NULL, GEMM row r
  *              reads A row a_rows[r] (the permutation gather fused into the load;
  *              A then holds the un-permuted rows).
- *   B          [E*Nb][K]; expert e's matrix is rows [e*Nb, (e+1)*Nb); B->tscale per
- *              tensor or per expert (SCALE_SEGMENT, nseg == E).
+ *   B          [E*Nb][K]; expert e's matrix is rows [e*Nb, (e+1)*Nb);
  *              Nb = N (EPI_NONE) or 2N (EPI_SWIGLU: rows [gate_e (N); up_e (N)]).
+ *              B->tscale: per tensor (SCALE_TENSOR); per expert (SCALE_SEGMENT,
+ *              nseg == E); per expert and projection (SCALE_SEGMENT, nseg == 2E,
+ *              EPI_SWIGLU only: gate_e has G[2e], up_e G[2e+1]); or per expert and
+ *              K half (SCALE_SEGMENT_HALVES, nseg == E, EPI_NONE, (K/2) % 128 == 0,
+ *              A scaled per tensor: products over K [0, K/2) take G[2e], over
+ *              [K/2, K) G[2e+1]; the accumulator is rescaled once by
+ *              fp32(G[2e] / G[2e+1]) at K/2, a single extra rounding).
  *   C          [M_cap][ldc] of ctype; rows [0, offsets[E]) are written.
  *   EPI_SWIGLU C = silu(gate) * up with silu(g) = g / (1 + exp(-g)), computed in
  *              FP32 after the tensor scales; amax_out (device FP32 [1], may be
@@ -277,7 +301,8 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
  * K (A->K == B->K) must be a positive multiple of 64: the kernel stages K in
  * 128-wide slices and reads 64-element halves; GROUP_K ranges only need 16.
  * Errors: EINVAL, EALIGN (K not a positive multiple of 64, A->K != B->K),
- * EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K), EWORKSPACE, EHIP.
+ * EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K, a B scale grouping
+ * other than those above), EWORKSPACE, EHIP.
  */
 size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K);
 nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
@@ -296,7 +321,8 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
  *
  * The source is either x (BF16 [x_rows][ldx], ldx >= K, ldx % 8 == 0, 16-byte
  * aligned) or q (an NVFP4 tensor [q->rows][K] with its tscale grouping: per
- * tensor, per equal segment of q->rows/q->nseg rows, or per row); exactly one is
+ * tensor, per equal segment of q->rows/q->nseg rows, or per row; not
+ * SCALE_SEGMENT_HALVES); exactly one is
  * non-NULL (with rows == 0 both may be NULL: nothing is read, and out may be NULL
  * when it has no elements).  The BF16 value of an NVFP4 element is
  *   bf16_rne(fp32(e2m1(q) * sf * G))

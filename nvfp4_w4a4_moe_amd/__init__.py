@@ -35,7 +35,7 @@ LIB_PATH = os.path.join(_HERE, "libnv4moe.so")
 # constants (mirror include/nv4moe.h)
 NV4_BF16, NV4_F32 = 0, 1
 NV4_ROWS, NV4_COLS, NV4_COLS_BATCHED, NV4_ROWS_AND_COLS = 1, 2, 3, 4
-NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT, NV4_SCALE_ROW = 0, 1, 2
+NV4_SCALE_TENSOR, NV4_SCALE_SEGMENT, NV4_SCALE_ROW, NV4_SCALE_SEGMENT_HALVES = 0, 1, 2, 3
 NV4_GROUP_M, NV4_GROUP_K = 0, 1
 NV4_EPI_NONE, NV4_EPI_SWIGLU = 0, 1
 NV4_RENORM = 1
@@ -79,6 +79,11 @@ _SIGS = {
                          _P]),
     "bf16_grouped_gemm": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P, _P, _SZ,
                                _P]),
+    # measurement kernels (include/nv4moe_bench.h)
+    "nv4_bench_copy": (_I, [_P, _P, _SZ, _P]),
+    "nv4_bench_read": (_I, [_P, _SZ, ctypes.c_uint32, _P, _P]),
+    "nv4_bench_mfma_out_floats": (_SZ, [_I]),
+    "nv4_bench_mfma": (_I, [_P, _I, _I, _P]),
 }
 
 
@@ -143,7 +148,13 @@ class NVFP4:
 
 
 def _ngroups(rows, scale_mode, nseg):
-    return 1 if scale_mode == NV4_SCALE_TENSOR else (nseg if scale_mode == NV4_SCALE_SEGMENT else rows)
+    if scale_mode == NV4_SCALE_TENSOR:
+        return 1
+    if scale_mode == NV4_SCALE_SEGMENT:
+        return nseg
+    if scale_mode == NV4_SCALE_SEGMENT_HALVES:
+        return 2 * nseg
+    return rows
 
 
 def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV4_SCALE_TENSOR, nseg: int = 1,
@@ -296,8 +307,9 @@ def moe_combine(Y: torch.Tensor, token_row: torch.Tensor, topk_w: torch.Tensor, 
 
 @dataclass
 class ExpertWeights:
-    """Quantised expert weights: W13 [E*2I, H] (rows gate_e then up_e) and W2 [E*H, I],
-    one tensor scale per expert and projection."""
+    """Quantised expert weights: W13 [E*2I, H] (rows gate_e then up_e; 2E scale
+    segments, gate_e with tscale[2e] and up_e with tscale[2e+1]) and W2 [E*H, I]
+    (one scale per expert): one tensor scale per expert and projection."""
     w13: NVFP4
     w2: NVFP4
     E: int
@@ -306,9 +318,10 @@ class ExpertWeights:
 
 
 def quantize_expert_weights(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> ExpertWeights:
-    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> NVFP4 with per-expert scales."""
+    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> NVFP4 with one scale per expert and
+    projection (gate, up and down)."""
     E, I2, H = W13.shape
-    w13 = nvfp4_quantize(W13.reshape(E * I2, H), scale_mode=NV4_SCALE_SEGMENT, nseg=E, stream=stream)
+    w13 = nvfp4_quantize(W13.reshape(E * I2, H), scale_mode=NV4_SCALE_SEGMENT, nseg=2 * E, stream=stream)
     w2 = nvfp4_quantize(W2.reshape(E * H, I2 // 2), scale_mode=NV4_SCALE_SEGMENT, nseg=E, stream=stream)
     return ExpertWeights(w13, w2, E, H, I2 // 2)
 
@@ -415,8 +428,9 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
 @dataclass
 class TransposedWeights:
     """Expert weights transposed and re-quantised along their new contraction
-    dimension (the operands of the data gradients): W2^T [E*I, H] and
-    W13^T [E*H, 2I], one tensor scale per expert and projection."""
+    dimension (the operands of the data gradients): W2^T [E*I, H] (one scale per
+    expert) and W13^T [E*H, 2I] (per expert, the gate scale on K [0, I) and the up
+    scale on [I, 2I)): one tensor scale per expert and projection."""
     w2t: NVFP4
     w13t: NVFP4
 
@@ -426,7 +440,7 @@ def quantize_expert_weights_t(W13: torch.Tensor, W2: torch.Tensor, stream=None) 
     E, I2, H = W13.shape
     w2t = nvfp4_quantize(W2.reshape(E * H, I2 // 2), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT,
                          nseg=E, stream=stream)
-    w13t = nvfp4_quantize(W13.reshape(E * I2, H), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT,
+    w13t = nvfp4_quantize(W13.reshape(E * I2, H), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT_HALVES,
                           nseg=E, stream=stream)
     return TransposedWeights(w2t, w13t)
 
@@ -753,3 +767,28 @@ def moe_backward_bf16(x_op, hact_op, wt: BF16TransposedWeights, dY2: torch.Tenso
         bf16_grouped_gemm(bufs.dy13c, bufs.xc, rt.padded_offsets, E, 2 * I, group_mode=NV4_GROUP_K, C=bufs.dw13,
                           ws=bufs.gemm_ws, stream=stream)
     return bufs
+
+
+# ----------------------------------------------------------------------------- measurement kernels
+
+def nv4_bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Stream-copy src into dst (same byte size, a multiple of 16): 2x the bytes of HBM traffic."""
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() == nb
+    _check(load().nv4_bench_copy(_ptr(src), _ptr(dst), nb, _stream(stream)))
+
+
+def nv4_bench_read(src: torch.Tensor, sink: torch.Tensor, never: int = 0xDEADBEEF, stream=None) -> None:
+    """Stream-read src (a pure read stream unless the XOR of its words equals `never`)."""
+    _check(load().nv4_bench_read(_ptr(src), src.numel() * src.element_size(), ctypes.c_uint32(never), _ptr(sink),
+                                 _stream(stream)))
+
+
+def nv4_bench_mfma(out: torch.Tensor | None, iters: int, waves_per_simd: int = 2, stream=None) -> tuple:
+    """A loop of FP16 MFMAs on every SIMD; returns (out, FLOPs of the call)."""
+    lib = load()
+    n = lib.nv4_bench_mfma_out_floats(waves_per_simd)
+    if out is None or out.numel() < n:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    _check(lib.nv4_bench_mfma(_ptr(out), iters, waves_per_simd, _stream(stream)))
+    return out, (n // 64) * iters * 8 * 32768

@@ -41,6 +41,7 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 int ngroups_of(int64_t rows, int scale_mode, int nseg) {
   if (scale_mode == NV4_SCALE_TENSOR) return 1;
   if (scale_mode == NV4_SCALE_SEGMENT) return nseg;
+  if (scale_mode == NV4_SCALE_SEGMENT_HALVES) return 2 * nseg;
   return (int)rows;
 }
 
@@ -116,8 +117,16 @@ static nv4_status quantize_impl(const void *x, nv4_dtype xtype, int64_t rows, in
     if (!aligned(out_rows->codes, 16) || !aligned(out_rows->scales, 4))
       return fail(NV4_EALIGN, "nvfp4_quantize: out_rows codes must be 16-byte and scales 4-byte aligned");
   }
-  if (scale_mode != NV4_SCALE_TENSOR && scale_mode != NV4_SCALE_SEGMENT && scale_mode != NV4_SCALE_ROW)
+  if (scale_mode != NV4_SCALE_TENSOR && scale_mode != NV4_SCALE_SEGMENT && scale_mode != NV4_SCALE_ROW &&
+      scale_mode != NV4_SCALE_SEGMENT_HALVES)
     return fail(NV4_EINVAL, "nvfp4_quantize: bad scale_mode %d", scale_mode);
+  if (scale_mode == NV4_SCALE_SEGMENT_HALVES) {
+    if (layout != NV4_COLS_BATCHED)
+      return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: NV4_SCALE_SEGMENT_HALVES needs the NV4_COLS_BATCHED layout");
+    if (seg_offsets) return fail(NV4_EINVAL, "nvfp4_quantize: NV4_SCALE_SEGMENT_HALVES takes no seg_offsets");
+    if (nseg <= 0 || rows % nseg || (rows / nseg) % 32)
+      return fail(NV4_EALIGN, "nvfp4_quantize: NV4_SCALE_SEGMENT_HALVES needs rows/nseg to be a multiple of 32");
+  }
   if (scale_mode == NV4_SCALE_ROW && layout != NV4_ROWS)
     return fail(NV4_EUNSUPPORTED, "nvfp4_quantize: per-row scales need the NV4_ROWS layout");
   if (row_index && layout == NV4_COLS_BATCHED)
@@ -165,7 +174,9 @@ static nv4_status quantize_impl(const void *x, nv4_dtype xtype, int64_t rows, in
     return fail(NV4_EWORKSPACE, "nvfp4_quantize: workspace of %zu bytes required", need);
 
   out->scale_mode = scale_mode;
-  out->nseg = scale_mode == NV4_SCALE_SEGMENT ? nseg : (scale_mode == NV4_SCALE_ROW ? (int32_t)rows : 1);
+  out->nseg = (scale_mode == NV4_SCALE_SEGMENT || scale_mode == NV4_SCALE_SEGMENT_HALVES)
+                  ? nseg
+                  : (scale_mode == NV4_SCALE_ROW ? (int32_t)rows : 1);
   if (rows == 0 || K == 0) {
     if (ng == 0) return ok();
   }
@@ -328,6 +339,7 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
   g.b_scales = B->scales;
   g.b_tscale = B->tscale;
   g.b_scale_mode = B->scale_mode;
+  g.b_nseg = B->nseg;
   g.b_rows = B->rows;
   g.offsets = offsets;
   g.E = E;
@@ -349,12 +361,25 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
     if (B->rows != (int64_t)E * Nb)
       return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B->rows = %lld, expected E * %lld", (long long)B->rows,
                   (long long)Nb);
-    if (A->scale_mode == NV4_SCALE_SEGMENT)
+    if (A->scale_mode != NV4_SCALE_TENSOR && A->scale_mode != NV4_SCALE_ROW)
       return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: A scales must be per tensor or per row");
-    if (B->scale_mode == NV4_SCALE_ROW)
-      return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: B scales must be per tensor or per expert");
-    if (B->scale_mode == NV4_SCALE_SEGMENT && B->nseg != E)
-      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B has %d scale segments, expected E = %d", B->nseg, E);
+    if (B->scale_mode == NV4_SCALE_SEGMENT) {
+      const bool swiglu2 = epilogue == NV4_EPI_SWIGLU && B->nseg == 2 * E;
+      if (B->nseg != E && !swiglu2)
+        return fail(NV4_EINVAL,
+                    "nvfp4_grouped_gemm: B has %d scale segments, expected E = %d (or 2E with the SwiGLU epilogue)",
+                    B->nseg, E);
+    } else if (B->scale_mode == NV4_SCALE_SEGMENT_HALVES) {
+      if (epilogue != NV4_EPI_NONE || A->scale_mode != NV4_SCALE_TENSOR)
+        return fail(NV4_EUNSUPPORTED,
+                    "nvfp4_grouped_gemm: per-K-half B scales need EPI_NONE and a per-tensor A scale");
+      if (B->nseg != E)
+        return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B has %d scale segments, expected E = %d", B->nseg, E);
+      if ((A->K / 2) % 128)
+        return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: per-K-half B scales need (K/2) %% 128 == 0");
+    } else if (B->scale_mode != NV4_SCALE_TENSOR) {
+      return fail(NV4_EUNSUPPORTED, "nvfp4_grouped_gemm: B scales must be per tensor, expert or projection");
+    }
     if (M_cap < 0 || (a_rows == nullptr && M_cap > A->rows))
       return fail(NV4_EINVAL, "nvfp4_grouped_gemm: M_cap exceeds the rows of A");
     if (ldc < N) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: ldc < N");
@@ -464,6 +489,8 @@ nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_ten
     if (row_index && rows > 0 && q->rows <= 0) return fail(NV4_EINVAL, "nv4_to_bf16: row index into an empty q");
     if (q->scale_mode == NV4_SCALE_SEGMENT && (q->nseg <= 0 || q->rows % q->nseg))
       return fail(NV4_EINVAL, "nv4_to_bf16: segment scales need q->rows % q->nseg == 0");
+    if (q->scale_mode == NV4_SCALE_SEGMENT_HALVES)
+      return fail(NV4_EUNSUPPORTED, "nv4_to_bf16: per-K-half scales are not supported as a source");
     if (q->scale_mode != NV4_SCALE_TENSOR && q->scale_mode != NV4_SCALE_SEGMENT && q->scale_mode != NV4_SCALE_ROW)
       return fail(NV4_EINVAL, "nv4_to_bf16: bad q->scale_mode");
     a.codes = q->codes;

@@ -224,7 +224,10 @@ __device__ __forceinline__ int64_t b_row_of(const GemmArgs &g, const TileJob &jo
   return col < g.N ? (int64_t)job.e * g.N + col : -1;
 }
 
-template <class Cfg, int GROUP, int EPI, bool OUT_F32, bool A_ROW_SCALE>
+// KSPLIT: B carries one decode scale per expert and K half (SCALE_SEGMENT_HALVES, GROUP_M,
+// (K/2) % BK == 0): the accumulators hold the first half's products scaled by
+// G[2e] / G[2e+1] when the second half starts, and G[2e+1] is applied at the end.
+template <class Cfg, int GROUP, int EPI, bool OUT_F32, bool A_ROW_SCALE, bool KSPLIT = false>
 __global__ __launch_bounds__(Cfg::kThreads) __attribute__((amdgpu_waves_per_eu(Cfg::kWavesPerSimd)))
 void k_gemm(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::kThreads, NW = NT / 64;
@@ -422,6 +425,25 @@ void k_gemm(GemmArgs g) {
       }
     };
 
+    // B decode scales of this tile (the same for every column of a tile): per tensor;
+    // per expert; gate and up of the expert (SwiGLU with 2E segments); or the two K
+    // halves of the expert (KSPLIT, applied as a ratio at K/2 and b_gate at the end)
+    float b_gate = 1.0f, b_up = 1.0f, k_ratio = 1.0f;
+    if (!BF) {
+      if (GROUP == NV4_GROUP_K || g.b_scale_mode == NV4_SCALE_TENSOR) {
+        b_gate = b_up = g.b_tscale[0];
+      } else if (KSPLIT) {
+        const float g0 = g.b_tscale[2 * job.e], g1 = g.b_tscale[2 * job.e + 1];
+        b_gate = b_up = g1;
+        k_ratio = __fdiv_rn(g0, g1);
+      } else if (EPI == NV4_EPI_SWIGLU && g.b_nseg == 2 * E) {
+        b_gate = g.b_tscale[2 * job.e];
+        b_up = g.b_tscale[2 * job.e + 1];
+      } else {
+        b_gate = b_up = g.b_tscale[job.e];
+      }
+    }
+
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -589,14 +611,36 @@ void k_gemm(GemmArgs g) {
       if constexpr (S == 2) {
         // pairs of stages with no branch between them, then the odd stage: with a
         // conditional second stage the accumulators were copied between registers
-        // on every iteration
+        // on every iteration.  Stage kt is in buffer kt % 2.
         int kt = 0;
+        if constexpr (KSPLIT) {
+          const int nks = (int)((K >> 1) / BK);  // stages of the first K half
+          for (; kt + 1 < nks; kt += 2) {
+            stage(0, kt);
+            stage(1, kt + 1);
+          }
+          if (kt < nks) {
+            stage(0, kt);
+            ++kt;
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[i][j][r] *= k_ratio;
+          if (kt & 1) {  // the second half starts in buffer 1
+            stage(1, kt);
+            ++kt;
+          }
+        }
         for (; kt + 1 < nk; kt += 2) {
           stage(0, kt);
           stage(1, kt + 1);
         }
         if (kt < nk) stage(0, kt);
       } else {
+        static_assert(!KSPLIT, "the K-half rescale is built for the two-stage ring");
         for (int kt = 0; kt < nk; kt += S) {
           stage(0, kt);
           if (kt + 1 < nk) stage(1, kt + 1);
@@ -611,10 +655,6 @@ void k_gemm(GemmArgs g) {
     block_barrier();
 
     // ---- epilogue: tensor scales, optional SwiGLU, store
-    float b_ts = 1.0f;
-    if (BF) b_ts = 1.0f;
-    else if (GROUP == NV4_GROUP_M) b_ts = g.b_scale_mode == NV4_SCALE_SEGMENT ? g.b_tscale[job.e] : g.b_tscale[0];
-    else b_ts = g.b_tscale[0];
     const int ldc = (int)g.ldc;
     int colw, ncols;  // first output column of this wave's fragment 0 (before the lane), column count
     if (EPI == NV4_EPI_SWIGLU) {
@@ -643,7 +683,7 @@ void k_gemm(GemmArgs g) {
       for (int q = 0; q < 4; ++q)
         voff[q][j] = col < ncols ? (uint32_t)(((q + h * 4) * ldc + col) * ESZ) : 0x80000000u;
     }
-    const float sc = a_ts * b_ts;
+    const float sc = a_ts * b_gate, sc_up = a_ts * b_up;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -657,13 +697,17 @@ void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = g4 * 4 + q;
-          float rsc = sc;
-          if (A_ROW_SCALE) rsc = row_scale[it & 1][wm * FM * 32 + ru + q + h * 4] * b_ts;
+          float rsc = sc, rsc_up = sc_up;
+          if (A_ROW_SCALE) {
+            const float ra = row_scale[it & 1][wm * FM * 32 + ru + q + h * 4];
+            rsc = ra * b_gate;
+            rsc_up = ra * b_up;
+          }
           if (EPI == NV4_EPI_SWIGLU) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
               const float gt = acc[i][j][r] * rsc;
-              const float up = acc[i][j + FN / 2][r] * rsc;
+              const float up = acc[i][j + FN / 2][r] * rsc_up;
               // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
               const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
               float stored;
@@ -718,7 +762,7 @@ __global__ void k_zero_counter(int32_t *p) {
   if (i == 0) p[i] = 0;
 }
 
-template <int GROUP, int EPI, bool OUT_F32, bool ROWS, class Cfg = GemmTile>
+template <int GROUP, int EPI, bool OUT_F32, bool ROWS, class Cfg = GemmTile, bool KSPLIT = false>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
   if (GROUP == NV4_GROUP_K && g.tile_counter) k_zero_counter<<<1, 64, 0, stream>>>(g.tile_counter);
   const int cus = device_cu_count();
@@ -727,7 +771,7 @@ hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
   int grid = cus * Cfg::kWavesPerSimd * 4 / (Cfg::kThreads / 64);
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
-  k_gemm<Cfg, GROUP, EPI, OUT_F32, ROWS><<<grid, Cfg::kThreads, 0, stream>>>(g);
+  k_gemm<Cfg, GROUP, EPI, OUT_F32, ROWS, KSPLIT><<<grid, Cfg::kThreads, 0, stream>>>(g);
   return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ struct GemmArgs {
   const uint8_t *b_codes, *b_scales;
   const float *b_tscale;
   int b_scale_mode;
+  int b_nseg;                    // scale segments of B (SCALE_SEGMENT: E, or 2E gate/up; HALVES: E)
   int64_t b_rows;
   const int32_t *offsets;
   int E;

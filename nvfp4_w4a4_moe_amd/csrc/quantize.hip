@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_rows(QuantArgs a, int P) {
   int64_t r0, r1;
   if (a.scale_mode == NV4_SCALE_TENSOR) { r0 = 0; r1 = a.rows; }
   else if (a.seg_offsets) { r0 = a.seg_offsets[g]; r1 = a.seg_offsets[g + 1]; }
-  else { const int64_t len = a.rows / a.nseg; r0 = (int64_t)g * len; r1 = r0 + len; }
+  else { const int64_t len = a.rows / a.ngroups; r0 = (int64_t)g * len; r1 = r0 + len; }  // equal segments
   const int64_t kc = a.K >> 3;
   const int64_t total = (r1 - r0) * kc;
   const int64_t stride = (int64_t)P * kThreads;
@@ -489,7 +489,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     orow0 = c0;
   }
   if (p0 >= plimit) return;  // uniform over the workgroup
-  const bool seg_scales = a.scale_mode == NV4_SCALE_SEGMENT;
+  // SCALE_SEGMENT_HALVES (batched only): positions [0, m/2) of matrix s take group
+  // 2s, [m/2, m) group 2s + 1 (the first and second half of the matrix's rows)
+  const bool halves = a.scale_mode == NV4_SCALE_SEGMENT_HALVES;
+  const bool seg_scales = a.scale_mode == NV4_SCALE_SEGMENT || halves;
   // per-block source rows: start, count (0..16), scale group
   if (threadIdx.x < NB) {
     const int j = threadIdx.x;
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
       if (batched) {
         start = (int64_t)s_tile * plimit + p;
         n = 16;
-        g = seg_scales ? s_tile : 0;
+        g = halves ? 2 * s_tile + (p >= plimit / 2 ? 1 : 0) : (seg_scales ? s_tile : 0);
       } else {
         int lo = 0, hi = a.nseg - 1;  // last segment s with pad[s] <= p
         while (lo < hi) {
@@ -517,8 +520,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     bgrp[j] = g;
   }
   // one tensor scale for the whole tile: 1 / block scale from a table
-  const bool uniform = !seg_scales || batched;
-  const float S_tile = tensor_encode_scale(A[uniform ? (seg_scales ? s_tile : 0) : 0]);
+  const bool straddle = halves && p0 < plimit / 2 && p0 + P > plimit / 2;
+  const bool uniform = (!seg_scales || batched) && !straddle;
+  const int tile_group = !seg_scales ? 0 : (halves ? 2 * s_tile + (p0 >= plimit / 2 ? 1 : 0) : s_tile);
+  const float S_tile = tensor_encode_scale(A[uniform ? tile_group : 0]);
   if (uniform && threadIdx.x < 128)
     inv_tab[threadIdx.x] = threadIdx.x ? __fdiv_rn(S_tile, e4m3_to_f32(threadIdx.x)) : 0.0f;
   __syncthreads();
@@ -682,7 +687,7 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
     if (a.rows > 0) {
       // about one workgroup per CU in total, split over the groups, at most one
       // per 2048 chunks of a group
-      const int groups = a.scale_mode == NV4_SCALE_TENSOR ? 1 : a.nseg;
+      const int groups = a.ngroups;
       const int64_t chunks_per_group = (a.rows + groups - 1) / groups * (a.K >> 3);
       const int P = (int)std::max<int64_t>(1, std::min<int64_t>(cus / groups, (chunks_per_group + 2047) / 2048));
       if (f32) k_amax_rows<true><<<dim3(P, groups), kThreads, 0, stream>>>(a, P);

@@ -34,6 +34,12 @@ def nvfp4_host(t, group_of_row=None) -> Q.NVFP4:
     scales = host(t.scales)
     G = host(t.tscale).astype(np.float32)
     rows = codes.shape[0]
+    if t.scale_mode == 3 and group_of_row is None:
+        # one scale per segment and K half: block b of row r takes 2 * segment + (b >= nblk / 2)
+        nblk = scales.shape[1]
+        seg = np.arange(rows) // (rows // t.nseg)
+        grp = 2 * seg[:, None] + (np.arange(nblk)[None, :] >= nblk // 2)
+        return Q.NVFP4(codes, scales, G[: 2 * t.nseg], G[grp], np.zeros(1, np.float32))
     if group_of_row is None:
         if t.scale_mode == 0:
             group_of_row = np.zeros(rows, np.int64)

@@ -1,6 +1,6 @@
-"""The C ABI without a GPU: the library loads, exports every function that
-include/nv4moe.h declares, and its host-side validation rejects bad arguments
-with the documented status before anything is launched."""
+"""The C ABI without a GPU: the library loads, exports every function that the
+headers under include/ declare, and its host-side validation rejects bad
+arguments with the documented status before anything is launched."""
 
 import ctypes
 import os
@@ -9,15 +9,18 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "nv4moe.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 nv4 = pytest.importorskip("nvfp4_w4a4_moe_amd")
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "while", "for", "sizeof")))
 
 
@@ -36,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"nv4_version", "nv4_status_string", "nv4_last_error", "nvfp4_quantize_workspace",
                           "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
                           "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
-                          "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr"}
+                          "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr",
+                          "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma"}
 
 
 def test_binding_covers_every_symbol():
@@ -76,6 +80,9 @@ def test_quantize_validation(lib):
     d = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 32, 64, 0, 1)
     assert lib.nvfp4_quantize(ctypes.c_void_p(0x1000), 0, 32, 64, 64, None, 1, 0, 1, None, None, None, None,
                               ctypes.byref(d), None, None, 0, None, None) == -4      # no workspace
+    # one scale per half of each matrix's rows: batched columns only, rows/nseg % 32 == 0
+    assert _q(lib, mode=3, nseg=1) == -3
+    assert _q(lib, layout=3, mode=3, nseg=2, orows=2 * 64, oK=16) == -2
     # rows-and-columns: tensor scale only, needs out_rows of the source shape
     assert _q(lib, layout=4, mode=1, nseg=2, orows=64, oK=128) == -3
     assert _q(lib, layout=4, orows=64, oK=128) == -1          # no out_rows
@@ -112,6 +119,19 @@ def test_gemm_validation(lib):
     a_seg = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 2048, 1, 8)
     assert g(a_seg, b) == -3
     assert g(a, b, E=0) == -1
+    # one scale per projection: 2E segments only with the SwiGLU epilogue (gate, up)
+    bn = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 768, 2048, 1, 16)
+    assert g(a, bn, epi=0) == -1
+    # one scale per K half: EPI_NONE, per-tensor A, (K/2) % 128 == 0
+    bh2 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 2048, 3, 8)
+    assert g(a, bh2, epi=1) == -3
+    bh = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 768, 2048, 3, 8)
+    a_row = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 2048, 2, 256)
+    assert g(a_row, bh, epi=0) == -3
+    a3 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 1536 + 64, 0, 1)
+    bh3 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 768, 1536 + 64, 3, 8)
+    assert g(a3, bh3, epi=0) == -3            # K/2 = 800 is not a whole number of 128-wide stages
+    assert b"K/2" in lib.nv4_last_error()
 
 
 def test_combine_validation(lib):

@@ -11,6 +11,7 @@ import torch
 import synth
 from oracle import moe
 from oracle import nvfp4 as Q
+from oracle import pipeline as P
 from tests.gpu_util import bf16_rne_of, dev_bf16, dev_f32, host, nvfp4_host, rel_frob
 
 pytestmark = pytest.mark.gpu
@@ -56,8 +57,11 @@ def test_tiny_backward_stagewise(gpu_lib, dual):
     _exact_rows(b.dy13q, Q.quantize_rows(d["dY13"]))
     assert host(b.dy2_amax)[0] == np.abs(d["dY2"]).max()
     # S8: expert weights transposed and quantised along the new K, one scale per expert
-    _exact_rows(wt.w2t, Q.quantize_cols_batched(d["W2"].reshape(E * H, I), E))
-    _exact_rows(wt.w13t, Q.quantize_cols_batched(d["W13"].reshape(E * 2 * I, H), E))
+    # (W13^T carries the gate scale on K [0, I) and the up scale on [I, 2I))
+    w2t_ref, w13t_ref = P.quantize_expert_weights_t(d["W13"], d["W2"])
+    _exact_rows(wt.w2t, w2t_ref)
+    _exact_rows(wt.w13t, w13t_ref)
+    assert wt.w13t.scale_mode == gpu_lib.NV4_SCALE_SEGMENT_HALVES and len(w13t_ref.G) == 2 * E
     # S9: data gradients on the GPU's own operands
     dh_ref = moe.grouped_gemm_m(nvfp4_host(b.dy2q).dequant(), nvfp4_host(wt.w2t).dequant(), off, E, I)
     assert rel_frob(host(b.dhact), dh_ref) <= TOL
@@ -103,12 +107,18 @@ def test_backward_is_bitwise_repeatable(gpu_lib):
 
 
 def _deq(t, rows, c0, c1, G):
-    """Dequantised block [rows][c0:c1] of a GPU NVFP4 tensor with one decode scale G
+    """Dequantised block [rows][c0:c1] of a GPU NVFP4 tensor with one decode scale G,
+    or with G = (G_lo, G_hi) the scales of the columns before and after (c0 + c1) / 2
     (sliced on the device, decoded by the oracle)."""
     idx = torch.as_tensor(np.asarray(rows, np.int64), device=t.codes.device)
     codes = Q.unpack_codes(host(t.codes.index_select(0, idx)[:, c0 // 2:c1 // 2].contiguous()))
     sc = host(t.scales.index_select(0, idx)[:, c0 // 16:c1 // 16].contiguous())
-    return Q.dequantize(codes, sc, np.full(sc.shape, G, np.float32)).astype(np.float64)
+    Gb = np.empty(sc.shape, np.float32)
+    if np.ndim(G) == 0:
+        Gb[:] = G
+    else:
+        Gb[:, : sc.shape[1] // 2], Gb[:, sc.shape[1] // 2:] = G[0], G[1]
+    return Q.dequantize(codes, sc, Gb).astype(np.float64)
 
 
 def _codes(t, rows, c0, c1):
@@ -152,7 +162,7 @@ def test_learner_shaped_backward_sampled(gpu_lib):
     for e in np.unique(e_of):
         m = e_of == e
         ref2[m] = dy2[m] @ _deq(wt.w2t, np.arange(e * I, (e + 1) * I), 0, H, w2tG[e]).T
-        ref13[m] = dy13[m] @ _deq(wt.w13t, np.arange(e * H, (e + 1) * H), 0, 2 * I, w13tG[e]).T
+        ref13[m] = dy13[m] @ _deq(wt.w13t, np.arange(e * H, (e + 1) * H), 0, 2 * I, w13tG[2 * e:2 * e + 2]).T
     idx = torch.as_tensor(rows, device=b.dhact.device)
     assert rel_frob(host(b.dhact.index_select(0, idx)), ref2) <= TOL
     assert rel_frob(host(b.dxperm.index_select(0, idx)), ref13) <= TOL

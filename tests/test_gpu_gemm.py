@@ -212,3 +212,59 @@ def test_combine_qwen_sampled(gpu_lib):
     w = host(rt.topk_w)[toks]
     ref = moe.combine(Y, tr, w)
     assert rel_frob(host(out)[toks], ref) <= TOL
+
+
+def test_gate_and_up_scales_per_projection(gpu_lib):
+    """One FP32 scale per expert projection ("The 4-bitter Lesson", "Why is the NVFP4
+    pretraining recipe not sufficient for RL?": one scale per weight tensor; footnote
+    5: three projections per expert), with up weights ~100x the gate weights so that
+    a swapped or shared scale is off by far more than the tolerance: the SwiGLU
+    epilogue applies G_gate to the gate and G_up to the up accumulators, and the data
+    gradient through the transposed W13 applies G_gate to K [0, I) and G_up to
+    [I, 2I) (one rescale at K = I)."""
+    cfg = synth.CONFIGS["tiny"]
+    E, H, I, R = cfg.E, cfg.H, cfg.I, cfg.R
+    d = synth.layer_inputs(cfg)
+    W13 = d["W13"].copy()
+    W13[:, I:] *= 100.0
+    W13 = synth.to_bf16_values(W13)
+    w = gpu_lib.quantize_expert_weights(dev_bf16(W13), dev_bf16(d["W2"]))
+    wt = gpu_lib.quantize_expert_weights_t(dev_bf16(W13), dev_bf16(d["W2"]))
+    xq = gpu_lib.nvfp4_quantize(dev_bf16(d["X"]))
+    rt = gpu_lib.moe_permute(dev_f32(d["logits"]), E, cfg.k)
+    G = host(w.w13.tscale)
+    assert (G[1::2] > 50 * G[0::2]).all()
+    C = gpu_lib.nvfp4_grouped_gemm(xq, w.w13, rt.offsets, E, I, M_cap=R, a_rows=rt.row_token,
+                                   epilogue=gpu_lib.NV4_EPI_SWIGLU)
+    ref = _swiglu_oracle(nvfp4_host(xq), nvfp4_host(w.w13), host(rt.row_token), host(rt.offsets), E, I)
+    assert rel_frob(host(C), ref) <= TOL
+    dy13 = synth.gradients((R, 2 * I), 55)
+    dyq = gpu_lib.nvfp4_quantize(dev_bf16(dy13))
+    dX = gpu_lib.nvfp4_grouped_gemm(dyq, wt.w13t, rt.offsets, E, H, M_cap=R)
+    ref = moe.grouped_gemm_m(nvfp4_host(dyq).dequant(), nvfp4_host(wt.w13t).dequant(), host(rt.offsets), E, H)
+    err = rel_frob(host(dX), ref)
+    print(f"dgrad through W13^T with per-half scales: rel Frobenius error {err:.3e}")
+    assert err <= TOL
+    # with one shared scale the error would be O(1): the test can see a swap
+    h = nvfp4_host(wt.w13t)
+    Gw = h.G_block.copy()
+    Gw[:, : I // 16] = Gw[:, I // 16:]                  # the up scale on both halves
+    wrong = moe.grouped_gemm_m(nvfp4_host(dyq).dequant(), Q.dequantize(h.codes, h.scales, Gw), host(rt.offsets), E, H)
+    assert rel_frob(wrong, ref) > 1e-2
+    dX16 = gpu_lib.nvfp4_grouped_gemm(dyq, wt.w13t, rt.offsets, E, H, M_cap=R, out_dtype=torch.bfloat16)
+    assert np.array_equal(host(dX16), bf16_rne_of(host(dX)))
+    dX2 = gpu_lib.nvfp4_grouped_gemm(dyq, wt.w13t, rt.offsets, E, H, M_cap=R)
+    assert torch.equal(dX.view(torch.int32), dX2.view(torch.int32))
+
+
+def test_per_half_scales_need_whole_stages(gpu_lib):
+    """A B operand with a scale per K half is accepted only where K/2 is a whole number
+    of 128-wide stages; otherwise the call fails on the host and launches nothing."""
+    E, I, H = 2, 80, 128
+    W13 = synth.weights((E, 2 * I, H), 57)
+    wt = gpu_lib.quantize_expert_weights_t(dev_bf16(W13), dev_bf16(synth.weights((E, H, I), 58)))
+    dyq = gpu_lib.nvfp4_quantize(dev_bf16(synth.gradients((64, 2 * I), 59)))
+    off = dev_i32(np.array([0, 30, 64]))
+    with pytest.raises(gpu_lib.NV4Error) as ei:
+        gpu_lib.nvfp4_grouped_gemm(dyq, wt.w13t, off, E, H, M_cap=64)
+    assert "NV4_EUNSUPPORTED" in str(ei.value) or "NV4_EALIGN" in str(ei.value)

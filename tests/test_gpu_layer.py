@@ -36,8 +36,10 @@ def test_tiny_forward_stagewise(gpu_lib, fuse_gather):
     assert np.array_equal(host(rt.topk_ids), ids) and np.array_equal(host(rt.row_token), p["row_token"])
     assert rel_frob(host(rt.topk_w), wts) <= TOL
     # S2 weights: exact
-    w13_ref = Q.quantize_rows(d["W13"].reshape(-1, cfg.H), "segment", nseg=cfg.E)
+    w13_ref, w2_ref = pipeline.quantize_expert_weights(d["W13"], d["W2"])   # one scale per projection
     assert np.array_equal(host(w.w13.codes), w13_ref.packed()) and np.array_equal(host(w.w13.tscale), w13_ref.G)
+    assert np.array_equal(host(w.w2.codes), w2_ref.packed()) and np.array_equal(host(w.w2.tscale), w2_ref.G)
+    assert len(w13_ref.G) == 2 * cfg.E
     # S4 GEMM1 + SwiGLU: FP32 variant vs oracle, stored BF16 == RNE(FP32 variant)
     h32 = gpu_lib.nvfp4_grouped_gemm(b.xq, w.w13, rt.offsets, cfg.E, cfg.I, M_cap=cfg.R, a_rows=rt.row_token,
                                      epilogue=gpu_lib.NV4_EPI_SWIGLU)
@@ -160,3 +162,72 @@ def test_captured_graph_replays_match_eager(gpu_lib):
         torch.cuda.synchronize()
         for a, b in zip(ref, outs()):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+
+
+def test_learner_forward_sampled(gpu_lib):
+    """The long-sequence learner batch's forward (65536 tokens, 128 experts, top-8,
+    skewed routing) in the launch configuration the benchmark times, stage by stage
+    on sampled rows, each oracle stage fed the GPU's own stage input: routing and
+    permutation exact; SwiGLU rows within 1e-5 (FP32 variant of the same call); the
+    quantised SwiGLU output bit-exact on sampled rows (amax of the whole stored
+    tensor); down-projection rows within 1e-5; combined tokens within 1e-5 and their
+    BF16 storage equal to the RNE of the FP32 combine."""
+    cfg = synth.CONFIGS["learner_64k"]
+    E, H, I, R, T = cfg.E, cfg.H, cfg.I, cfg.R, cfg.T
+    d = synth.layer_inputs(cfg)
+    w = gpu_lib.quantize_expert_weights(dev_bf16(d["W13"]), dev_bf16(d["W2"]))
+    x, lg = dev_bf16(d["X"]), dev_f32(d["logits"])
+    b = gpu_lib.moe_forward(x, lg, w, cfg.k)
+    torch.cuda.synchronize()
+    rt = b.routing
+    ids, _ = moe.route_topk(d["logits"], cfg.k)
+    p = moe.permute(ids, E)
+    assert np.array_equal(host(rt.topk_ids), ids) and np.array_equal(host(rt.offsets), p["offsets"])
+    assert np.array_equal(host(rt.row_token), p["row_token"])
+    off = p["offsets"].astype(np.int64)
+    r = synth.rng(17)
+    rows = np.sort(r.choice(R, 192, replace=False))
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    idx = torch.as_tensor(rows, device="cuda")
+    # S1 on the sampled tokens' rows (the whole tensor is pinned at this size elsewhere)
+    xq = nvfp4_host(b.xq)
+    # S4: FP32 variant of GEMM1 + SwiGLU, sampled rows; the stored BF16 is its RNE
+    h32 = gpu_lib.nvfp4_grouped_gemm(b.xq, w.w13, rt.offsets, E, I, M_cap=R, a_rows=rt.row_token,
+                                     epilogue=gpu_lib.NV4_EPI_SWIGLU)
+    w13 = nvfp4_host(w.w13)
+    w2 = nvfp4_host(w.w2)
+    tk = p["row_token"][rows]
+    A = Q.dequantize(xq.codes[tk], xq.scales[tk], xq.G_block[tk])
+    ref_h = np.zeros((len(rows), I))
+    for e in np.unique(e_of):
+        m = e_of == e
+        sl = slice(e * 2 * I, (e + 1) * 2 * I)
+        ref_h[m] = moe.swiglu(A[m] @ Q.dequantize(w13.codes[sl], w13.scales[sl], w13.G_block[sl]).T)
+    got_h32 = host(h32.index_select(0, idx))
+    assert rel_frob(got_h32, ref_h) <= TOL
+    assert np.array_equal(host(b.hact.index_select(0, idx)), bf16_rne_of(got_h32))
+    # S5: the epilogue's amax is the amax of the whole stored tensor; sampled rows exact
+    hact = host(b.hact)
+    assert host(b.hamax)[0] == np.abs(hact).max()
+    hq_ref = Q.quantize_rows(hact[rows], amax=np.abs(hact).max())
+    assert np.array_equal(host(b.hq.codes.index_select(0, idx)), hq_ref.packed())
+    assert np.array_equal(host(b.hq.scales.index_select(0, idx)), hq_ref.scales)
+    assert host(b.hq.tscale)[0] == hq_ref.G[0]
+    del hact
+    # S6: down projection on the GPU's quantised SwiGLU rows
+    Hd = Q.dequantize(hq_ref.codes, hq_ref.scales, hq_ref.G_block)
+    ref_y = np.zeros((len(rows), H))
+    for e in np.unique(e_of):
+        m = e_of == e
+        sl = slice(e * H, (e + 1) * H)
+        ref_y[m] = Hd[m] @ Q.dequantize(w2.codes[sl], w2.scales[sl], w2.G_block[sl]).T
+    assert rel_frob(host(b.y.index_select(0, idx)), ref_y) <= TOL
+    # S7: sampled tokens, from the GPU's expert rows
+    toks = np.sort(r.choice(T, 96, replace=False))
+    tr = host(rt.token_row)[toks]
+    ysel = host(b.y.index_select(0, torch.as_tensor(tr.reshape(-1).astype(np.int64), device="cuda")))
+    ref_o = moe.combine(ysel, np.arange(tr.size).reshape(tr.shape), host(rt.topk_w)[toks])
+    o32 = gpu_lib.moe_combine(b.y, rt.token_row, rt.topk_w)
+    got = host(o32)[toks]
+    assert rel_frob(got, ref_o) <= TOL
+    assert np.array_equal(host(b.out)[toks], bf16_rne_of(got))

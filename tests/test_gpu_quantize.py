@@ -6,7 +6,9 @@ import pytest
 import torch
 
 import synth
+from oracle import formats as F
 from oracle import nvfp4 as Q
+from oracle import pipeline as P
 from tests.gpu_util import dev_bf16, dev_f32, dev_i32, host, same_bits
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +49,57 @@ def test_weights_per_expert_scale(gpu_lib):
     _assert_exact(t, Q.quantize_rows(W13.reshape(-1, cfg.H), "segment", nseg=cfg.E))
     t = gpu_lib.nvfp4_quantize(dev_bf16(W2.reshape(-1, cfg.I)), scale_mode=gpu_lib.NV4_SCALE_SEGMENT, nseg=cfg.E)
     _assert_exact(t, Q.quantize_rows(W2.reshape(-1, cfg.I), "segment", nseg=cfg.E))
+
+
+def test_weights_one_scale_per_projection(gpu_lib):
+    """S2 and the weight transposes of S8 with one FP32 scale per expert and projection
+    (gate, up, down), gate and up amax about 100x apart: W13 in 2E row segments, W13^T
+    with a scale per K half (including a K half that is not a multiple of the 128-row
+    tile, so a tile straddles the two scale groups), all bit-exact."""
+    for E, I, H in ((8, 128, 256), (3, 80, 96)):
+        W13 = synth.weights((E, 2 * I, H), 60 + I)
+        W13[:, I:] *= 100.0
+        W13 = synth.to_bf16_values(W13)
+        W2 = synth.weights((E, H, I), 61 + I)
+        ref13, ref2 = P.quantize_expert_weights(W13, W2)
+        ref2t, ref13t = P.quantize_expert_weights_t(W13, W2)
+        w = gpu_lib.quantize_expert_weights(dev_bf16(W13), dev_bf16(W2))
+        wt = gpu_lib.quantize_expert_weights_t(dev_bf16(W13), dev_bf16(W2))
+        _assert_exact(w.w13, ref13)
+        _assert_exact(w.w2, ref2)
+        _assert_exact(wt.w2t, ref2t)
+        _assert_exact(wt.w13t, ref13t)
+        assert w.w13.nseg == 2 * E and wt.w13t.scale_mode == gpu_lib.NV4_SCALE_SEGMENT_HALVES
+        G = host(w.w13.tscale)
+        assert (G[1::2] > 50 * G[0::2]).all()
+
+
+def test_weights_full_size_sampled_experts(gpu_lib):
+    """S2 at the Qwen3-30B-A3B expert shapes (128 experts, hidden 2048, intermediate
+    768): all 384 tensor scales exact, and every byte of four experts' gate, up and
+    down matrices and of their transposes exact."""
+    cfg = synth.CONFIGS["learner_64k"]
+    E, H, I = cfg.E, cfg.H, cfg.I
+    W13, W2 = synth.expert_weights(cfg)
+    w = gpu_lib.quantize_expert_weights(dev_bf16(W13), dev_bf16(W2))
+    wt = gpu_lib.quantize_expert_weights_t(dev_bf16(W13), dev_bf16(W2))
+    torch.cuda.synchronize()
+    a13 = np.abs(W13.reshape(2 * E, I * H)).max(axis=1)
+    a2 = np.abs(W2.reshape(E, H * I)).max(axis=1)
+    G13 = Q.tensor_scales(a13)[1]
+    G2 = Q.tensor_scales(a2)[1]
+    assert np.array_equal(host(w.w13.tscale).view(np.uint32), G13.view(np.uint32))
+    assert np.array_equal(host(w.w2.tscale).view(np.uint32), G2.view(np.uint32))
+    assert np.array_equal(host(wt.w13t.tscale).view(np.uint32), G13.view(np.uint32))
+    assert np.array_equal(host(wt.w2t.tscale).view(np.uint32), G2.view(np.uint32))
+    for e in (0, 37, 90, 127):
+        r13, r2 = P.quantize_expert_weights(W13[e:e + 1], W2[e:e + 1])
+        r2t, r13t = P.quantize_expert_weights_t(W13[e:e + 1], W2[e:e + 1])
+        sl = lambda t, a, b: (host(t.codes[a:b]), host(t.scales[a:b]))
+        for t, ref, a, b in ((w.w13, r13, e * 2 * I, (e + 1) * 2 * I), (w.w2, r2, e * H, (e + 1) * H),
+                             (wt.w13t, r13t, e * H, (e + 1) * H), (wt.w2t, r2t, e * I, (e + 1) * I)):
+            c, sc = sl(t, a, b)
+            assert np.array_equal(c, ref.packed()) and np.array_equal(sc, ref.scales)
 
 
 def test_segment_offsets_with_empty_segments(gpu_lib):
@@ -182,3 +235,92 @@ def test_rows_and_columns_with_row_gather(gpu_lib):
     Kp = int(po[-1])
     assert np.array_equal(host(t.codes)[:, : Kp // 2], ref_c.packed())
     _assert_exact(t.rows_out, Q.quantize_rows(xg))
+
+
+# ---------------------------------------------------------------- rounding edge cases
+# The bytes are decided by two round-to-nearest-even steps ("The 4-bitter Lesson",
+# section "Improving Gradient Stability", footnote 6: clip(round(w/s))): the E4M3
+# block scale and the E2M1 element.  Random data almost never lands on a tie, so
+# these inputs are built to: the GPU must give the oracle's bytes on every one.
+
+def _tie_tensor() -> np.ndarray:
+    """Rows of 16-element blocks under one tensor scale S = 1 (the amax is 2688 = 6 *
+    448): every E4M3 midpoint as a block scale t_b (block max 6 m, exact in FP32 and
+    BF16), blocks with power-of-two scales 2^j holding every E2M1 midpoint times 2^j
+    (exact ties of v), values just above 6 (saturation), signed zeros and negative
+    values that round to zero."""
+    e4 = F.e4m3_finite_nonneg().astype(np.float64)                 # 127 values, 0 .. 448
+    mids = (e4[:-1] + e4[1:]) / 2
+    blocks = [[2688.0, 1344.0, -448.0, 0.0] + [0.0] * 12]
+    r = np.random.default_rng(3)
+    for m in mids:                                                 # t_b = m exactly: E4M3 ties
+        a = 6 * m
+        blocks.append([a, -a] + list(a * r.choice([0.5, 0.25, 0.75, 1 / 3, 0.9, 0.1, 1.0], 14)))
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for j in range(-9, 9):                                         # sf = 2^j exactly: E2M1 ties
+        s = 2.0 ** j
+        blocks.append(list(np.concatenate([[6.0], ties, [-6.0], -ties]) * s))
+        blocks.append(list(np.array([6.25, 6.125, -6.25, 5.5, 4.5, 0.0, -0.0, 1e-3, -1e-3] + [0.5] * 7) * s))
+    blocks.append([-0.0] * 8 + [0.0] * 8)                           # a zero block: sf 0, signs kept
+    blocks.append([-0.0, 0.0] + [-1e-30] * 7 + [1e-30] * 7)        # sf 0 (t_b below half the smallest subnormal)
+    x = np.array(blocks, np.float64).astype(np.float32)
+    nb = len(blocks)
+    per_row = 8
+    pad = (-nb) % per_row
+    x = np.vstack([x, np.zeros((pad, 16), np.float32)])
+    # BF16 values throughout (the tie values have at most 7 significant bits and stay exact)
+    xb = synth.to_bf16_values(x)
+    assert np.array_equal(xb[1:127, 0], x[1:127, 0]) and np.array_equal(xb[127:163:2], x[127:163:2])
+    return xb.reshape(-1, per_row * 16)
+
+
+@pytest.mark.parametrize("xdtype", ["f32", "bf16"])
+def test_rounding_ties_exact(gpu_lib, xdtype):
+    x = _tie_tensor()
+    ref = Q.quantize_rows(x)
+    assert ref.G[0] == 1.0
+    xd = dev_f32(x) if xdtype == "f32" else dev_bf16(x)
+    t = gpu_lib.nvfp4_quantize(xd)
+    _assert_exact(t, ref)
+    # the cases are really there: every E4M3 tie went to the even code, E2M1 ties too
+    sc = ref.scales.reshape(-1)
+    assert (sc[1:127] % 2 == 0).all()
+    assert ((ref.codes.reshape(-1, 16)[127] & 7)[1:8] == [0, 2, 2, 4, 4, 6, 6]).all()
+
+
+def test_every_bf16_amax_per_row_exact(gpu_lib):
+    """NV4_SCALE_ROW over every positive finite BF16 magnitude A as its row's amax
+    (32639 rows): the GPU matches the oracle byte for byte, and where 2688/A is finite
+    the block holding A has scale 448 (0x7E) and code 6 (0x7)."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    A = F.bf16_bits_to_f32(bits.astype(np.uint16))
+    x = np.zeros((len(A), 32), np.float32)
+    x[:, 0] = A
+    x[:, 1] = -A
+    x[:, 5] = F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32(A / np.float32(3))))
+    x[:, 20] = F.bf16_bits_to_f32(F.f32_to_bf16_bits(F.f32(A * np.float32(0.75))))
+    ref = Q.quantize_rows(x, "row")
+    t = gpu_lib.nvfp4_quantize(dev_bf16(x), scale_mode=gpu_lib.NV4_SCALE_ROW)
+    _assert_exact(t, ref)
+    finite = np.float64(2688.0) / A.astype(np.float64) < np.finfo(np.float32).max
+    sc = host(t.scales)
+    assert (sc[finite, 0] == 0x7E).all() and ((host(t.codes)[finite, 0] & 0xF) == 7).all()
+
+
+def test_columns_with_segment_scales_exact(gpu_lib):
+    """NV4_COLS with one scale per segment (the per-block scale-group branch of the
+    column kernel): ragged segments, one with an amax 40x the others, an empty one,
+    a one-row one, columns not a multiple of the tile."""
+    x = synth.activations(300, 96, 41)
+    off = np.array([0, 70, 70, 71, 200, 300])
+    x[71:200] *= 40.0
+    x = synth.to_bf16_values(x)
+    po = Q.padded_offsets(off)
+    t = gpu_lib.nvfp4_quantize(dev_bf16(x), layout=gpu_lib.NV4_COLS, scale_mode=gpu_lib.NV4_SCALE_SEGMENT,
+                               nseg=5, seg_offsets=dev_i32(off), seg_padded_offsets=dev_i32(po))
+    ref, _ = Q.quantize_cols(x, off, "segment")
+    Kp = int(po[-1])
+    assert np.array_equal(host(t.codes)[:, : Kp // 2], ref.packed())
+    assert np.array_equal(host(t.scales)[:, : Kp // 16], ref.scales)
+    assert np.array_equal(host(t.tscale).view(np.uint32), ref.G.view(np.uint32))
+    assert len(set(ref.G.tolist())) >= 3
