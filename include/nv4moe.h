@@ -259,6 +259,28 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
                        void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace, the same results bit for
+ * bit.  Its workspace is a static device array of moe_permute_noalloc_max_workspace()
+ * bytes (16 MiB) per GPU, held from the library's first use on that GPU until the
+ * process ends; the call allocates nothing.  Every call on one GPU shares that
+ * array, so calls that may overlap on one GPU (different streams without ordering)
+ * race and give unspecified results; calls on one stream are safe.  Nothing in the
+ * array needs clearing: every call writes each word it later reads.
+ * Errors: as moe_permute; NV4_EWORKSPACE (before anything is enqueued) when
+ * moe_permute_workspace(T, E, k) exceeds the static size -- T * k up to about
+ * 3.7 million assignments at E = 128.
+ */
+size_t moe_permute_noalloc_max_workspace(void);
+nv4_status moe_permute_noalloc(const float *logits, int64_t T, int E, int k, int flags,
+                               int32_t *topk_ids, float *topk_w,
+                               int32_t *expert_offsets, int32_t *padded_offsets,
+                               int32_t *row_token, int32_t *token_row,
+                               const nv4_tensor *gather_src, nv4_tensor *gather_dst,
+                               int32_t *dev_status, void *stream);
+
+/*
  * nvfp4_grouped_gemm -- one grouped GEMM over experts, C = A_hat . B_hat^T per
  * expert, both operands NVFP4 (W4A4).  [LBP] "What W4A4 GEMM Actually Changes"
  * (both operands 4-bit, the GEMM runs on the 4-bit data); [MTE] "Development:

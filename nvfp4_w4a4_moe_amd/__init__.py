@@ -71,6 +71,9 @@ _SIGS = {
     "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
     "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                          ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
+    "moe_permute_noalloc_max_workspace": (_SZ, []),
+    "moe_permute_noalloc": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
+                                 ctypes.POINTER(NV4Tensor), _P, _P]),
     "nvfp4_grouped_gemm_workspace": (_SZ, [_I, _I, _I64, _I64, _I64]),
     "nvfp4_grouped_gemm": (_I, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _P, _I, _I64, _I64, _P,
                                 _I, _I, _P, _I, _I64, _P, _P, _SZ, _P]),
@@ -253,6 +256,29 @@ def moe_permute(logits: torch.Tensor | None, E: int, k: int, T: int | None = Non
                            _ptr(padded), _ptr(row_token), _ptr(token_row), gs, gd, _ptr(ws), ws.numel(),
                            _ptr(dev_status), _stream(stream)))
     return Routing(topk_ids, topk_w, offsets, padded, row_token, token_row)
+
+
+def moe_permute_noalloc(logits: torch.Tensor | None, E: int, k: int, out: Routing, T: int | None = None,
+                        flags: int = 0, topk_ids: torch.Tensor | None = None,
+                        gather_src: NVFP4 | None = None, gather_dst: NVFP4 | None = None,
+                        dev_status: torch.Tensor | None = None, stream=None) -> Routing:
+    """moe_permute without a workspace (the library's static one) into the caller's
+    preallocated Routing buffers `out`: nothing is allocated, by the binding or the
+    library, so the call can run under HIP graph capture or in a serving loop."""
+    lib = load()
+    if logits is not None:
+        assert logits.dtype == torch.float32 and logits.is_contiguous() and logits.shape[1] == E
+        T = logits.shape[0]
+    elif topk_ids is not None:
+        T = topk_ids.shape[0]
+    ids = topk_ids if topk_ids is not None else out.topk_ids
+    gs = ctypes.byref(gather_src.c()) if gather_src is not None else None
+    gd = ctypes.byref(gather_dst.c()) if gather_dst is not None else None
+    _check(lib.moe_permute_noalloc(_ptr(logits), T, E, k, flags, _ptr(ids),
+                                   _ptr(out.topk_w) if logits is not None else None, _ptr(out.offsets),
+                                   _ptr(out.padded_offsets), _ptr(out.row_token), _ptr(out.token_row), gs, gd,
+                                   _ptr(dev_status), _stream(stream)))
+    return Routing(ids, out.topk_w, out.offsets, out.padded_offsets, out.row_token, out.token_row)
 
 
 def _gemm_ws(ws, group_mode, device):

@@ -298,6 +298,31 @@ nv4_status moe_permute(const float *logits, int64_t T, int E, int k, int flags,
   return from_hip(nv4::launch_permute(a, static_cast<hipStream_t>(stream)), "moe_permute");
 }
 
+nv4_status moe_permute_noalloc(const float *logits, int64_t T, int E, int k, int flags,
+                               int32_t *topk_ids, float *topk_w,
+                               int32_t *expert_offsets, int32_t *padded_offsets,
+                               int32_t *row_token, int32_t *token_row,
+                               const nv4_tensor *gather_src, nv4_tensor *gather_dst,
+                               int32_t *dev_status, void *stream) {
+  // the size check comes first: a call that does not fit touches no device
+  if (T < 0 || E <= 0 || k <= 0 || E > 1024 || k > 32 || T * (int64_t)k >= (1ll << 31))
+    return moe_permute(logits, T, E, k, flags, topk_ids, topk_w, expert_offsets, padded_offsets, row_token,
+                       token_row, gather_src, gather_dst, nullptr, 0, dev_status, stream);  // reports the error
+  const size_t need = nv4::permute_workspace_bytes(T, E, k);
+  if (need > nv4::kPermuteStaticBytes)
+    return fail(NV4_EWORKSPACE,
+                "moe_permute_noalloc: T = %lld, E = %d, k = %d needs %zu bytes of workspace, above the static %zu; "
+                "use moe_permute with a caller workspace",
+                (long long)T, E, k, need, nv4::kPermuteStaticBytes);
+  void *ws = nullptr;
+  const hipError_t e = nv4::permute_static_workspace(&ws);
+  if (e != hipSuccess) return from_hip(e, "moe_permute_noalloc: static workspace");
+  return moe_permute(logits, T, E, k, flags, topk_ids, topk_w, expert_offsets, padded_offsets, row_token,
+                     token_row, gather_src, gather_dst, ws, nv4::kPermuteStaticBytes, dev_status, stream);
+}
+
+size_t moe_permute_noalloc_max_workspace(void) { return nv4::kPermuteStaticBytes; }
+
 // ---------------------------------------------------------------- grouped GEMM
 
 size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K) {

@@ -52,6 +52,11 @@ struct PermuteArgs {
 };
 size_t permute_workspace_bytes(int64_t T, int E, int k);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream);
+// moe_permute_noalloc: the device address of this device's static workspace of
+// kPermuteStaticBytes (looked up once per device, then cached)
+constexpr size_t kPermuteStaticBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t permute_static_workspace(void **ptr);
 
 // ---------------------------------------------------------------- grouped GEMM
 struct GemmArgs {

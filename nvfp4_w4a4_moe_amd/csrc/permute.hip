@@ -19,6 +19,7 @@
 //   3. every assignment's row is base + local rank; a scatter writes the maps.
 // The result is one exactly defined permutation, identical on every run.
 #include <algorithm>
+#include <mutex>
 
 #include "nv4_device.h"
 #include "nv4_internal.h"
@@ -264,6 +265,30 @@ size_t permute_workspace_bytes(int64_t T, int E, int k) {
   const size_t a = (size_t)nchunks * E * sizeof(int32_t);
   const size_t b = (size_t)std::max<int64_t>(R, 1) * sizeof(int32_t);
   return ((a + 255) & ~(size_t)255) + ((b + 255) & ~(size_t)255);
+}
+
+// Workspace of moe_permute_noalloc: one array per device, for callers that cannot
+// allocate.  Host code never passes `scratch` itself to a kernel (on the host it
+// is a stand-in symbol, not a device address): the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[kPermuteStaticBytes];
+
+hipError_t permute_static_workspace(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream) {

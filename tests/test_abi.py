@@ -40,7 +40,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
                           "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
                           "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr",
-                          "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma"}
+                          "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma",
+                          "moe_permute_noalloc", "moe_permute_noalloc_max_workspace"}
 
 
 def test_binding_covers_every_symbol():
@@ -185,3 +186,16 @@ def test_quantize_sr_validates_like_quantize(lib):
                                                    None, ctypes.c_uint64(7), None)
     assert q(K=40, ldx=40) == -2
     assert q(ldx=32) == -1
+
+
+def test_permute_noalloc_rejects_sizes_above_its_static_workspace(lib):
+    """Checked on the host before the device is touched: a routing whose workspace
+    would not fit the static array fails with NV4_EWORKSPACE and a clear message."""
+    P = ctypes.c_void_p(0x1000)
+    cap = lib.moe_permute_noalloc_max_workspace()
+    assert cap == 16 << 20
+    T = 4_000_000 // 8
+    assert lib.moe_permute_workspace(T, 128, 8) > cap
+    rc = lib.moe_permute_noalloc(None, T, 128, 8, 0, P, P, P, P, P, P, None, None, None, None)
+    assert rc == -4 and b"moe_permute_noalloc" in lib.nv4_last_error()
+    assert lib.moe_permute_noalloc(None, 16, 2000, 2, 0, P, P, P, P, P, P, None, None, None, None) == -3
