@@ -392,6 +392,15 @@ def alloc_forward(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat
         hq_ws=torch.empty(256, dtype=torch.uint8, device=device))
 
 
+class StageEvents(list):
+    """A list for ``stage_events`` that also runs ``before()`` (for example a cache
+    eviction) on the launch stream ahead of every stage, outside the stage's events."""
+
+    def __init__(self, before=None):
+        super().__init__()
+        self.before = before
+
+
 class _Stage:
     """Optional per-stage timing: HIP events recorded on the launch stream."""
 
@@ -400,6 +409,10 @@ class _Stage:
 
     def __enter__(self):
         if self.events is not None:
+            before = getattr(self.events, "before", None)
+            if before is not None:
+                with torch.cuda.stream(self.stream):
+                    before()
             self.t0 = torch.cuda.Event(enable_timing=True)
             self.t0.record(self.stream)
 
