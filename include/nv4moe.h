@@ -313,20 +313,27 @@ nv4_status moe_permute_noalloc(const float *logits, int64_t T, int E, int k, int
  *   C [E][N][ldc] (ldc >= M) gets A_e . B_e^T; an empty range gives zeros.
  *   Tensor scales per tensor.
  *   offsets    device int32 [E+1].
- * ws, ws_bytes   optional device workspace (nvfp4_grouped_gemm_workspace() bytes,
- *              4-byte aligned; NULL or 0 is allowed).  With it, GROUP_K workgroups
- *              take tiles from a counter in the workspace, the largest experts'
- *              first, which balances skewed expert sizes; without it every
- *              workgroup walks a fixed share of the tiles.  Every tile is computed
- *              whole by one workgroup either way, so the output is bitwise the same.
+ * ws, ws_bytes   device workspace of nvfp4_grouped_gemm_workspace(A, B, group_mode) bytes
+ *              (256-byte aligned; NULL or 0 is allowed when that query returns 0, and for
+ *              GROUP_K with K % 64 == 0, where it only enables the tile counter below):
+ *              - GROUP_K: workgroups take tiles from a counter in the first word of the
+ *                workspace, the largest experts' first, which balances skewed expert
+ *                sizes; without it every workgroup walks a fixed share of the tiles.
+ *                Every tile is computed whole by one workgroup either way, so the output
+ *                is bitwise the same.
+ *              - K % 64 != 0 (either group mode): both operands are first copied into
+ *                the workspace with K zero-padded to the next multiple of 64 (the extra
+ *                blocks get scale 0 and add exact zeros to the FP32 sums), then the
+ *                kernel runs on the copies.
  *              Calls that share a workspace must not overlap.
- * K (A->K == B->K) must be a positive multiple of 64: the kernel stages K in
- * 128-wide slices and reads 64-element halves; GROUP_K ranges only need 16.
- * Errors: EINVAL, EALIGN (K not a positive multiple of 64, A->K != B->K),
- * EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K, a B scale grouping
- * other than those above), EWORKSPACE, EHIP.
+ * K (A->K == B->K) must be a positive multiple of 16 ([4BL] "Baseline": blocks of 16);
+ * GROUP_K ranges must be 16-aligned.
+ * Errors: EINVAL, EALIGN (K not a positive multiple of 16, A->K != B->K, misaligned
+ * codes), EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K, a B scale
+ * grouping other than those above), EWORKSPACE (K % 64 != 0 without the workspace),
+ * EHIP.
  */
-size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K);
+size_t nvfp4_grouped_gemm_workspace(const nv4_tensor *A, const nv4_tensor *B, int group_mode);
 nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
                               int64_t M_cap, int64_t N, const int32_t *a_rows,
                               int group_mode, int epilogue,

@@ -74,7 +74,7 @@ _SIGS = {
     "moe_permute_noalloc_max_workspace": (_SZ, []),
     "moe_permute_noalloc": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                                  ctypes.POINTER(NV4Tensor), _P, _P]),
-    "nvfp4_grouped_gemm_workspace": (_SZ, [_I, _I, _I64, _I64, _I64]),
+    "nvfp4_grouped_gemm_workspace": (_SZ, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _I]),
     "nvfp4_grouped_gemm": (_I, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _P, _I, _I64, _I64, _P,
                                 _I, _I, _P, _I, _I64, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I64, _I, _I64, _P, _I, _P]),
@@ -281,11 +281,18 @@ def moe_permute_noalloc(logits: torch.Tensor | None, E: int, k: int, out: Routin
     return Routing(ids, out.topk_w, out.offsets, out.padded_offsets, out.row_token, out.token_row)
 
 
-def _gemm_ws(ws, group_mode, device):
-    """The GROUP_K tile-schedule workspace: the caller's, else a new one."""
-    if group_mode != NV4_GROUP_K:
-        return None
-    return ws if ws is not None else torch.empty(256, dtype=torch.uint8, device=device)
+def _gemm_ws(ws, group_mode, device, A: "NVFP4 | None" = None, B: "NVFP4 | None" = None):
+    """The grouped GEMM's workspace (GROUP_K tile counter; repacked operands when K % 64
+    != 0): the caller's when it is large enough, else a new one."""
+    need = 256 if group_mode == NV4_GROUP_K else 0
+    if A is not None and B is not None:
+        a, b = A.c(), B.c()
+        need = load().nvfp4_grouped_gemm_workspace(ctypes.byref(a), ctypes.byref(b), group_mode)
+    if need == 0:
+        return ws
+    if ws is not None and ws.numel() >= need:
+        return ws
+    return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def nvfp4_grouped_gemm(A: NVFP4, B: NVFP4, offsets: torch.Tensor, E: int, N: int, M_cap: int | None = None,
@@ -310,7 +317,7 @@ def nvfp4_grouped_gemm(A: NVFP4, B: NVFP4, offsets: torch.Tensor, E: int, N: int
         ldc = C.stride(1)
         M_cap = 0
     a, b = A.c(), B.c()
-    ws = _gemm_ws(ws, group_mode, A.codes.device)
+    ws = _gemm_ws(ws, group_mode, A.codes.device, A, B)
     _check(lib.nvfp4_grouped_gemm(ctypes.byref(a), ctypes.byref(b), _ptr(offsets), E, M_cap, N, _ptr(a_rows),
                                   group_mode, epilogue, _ptr(C), _dtype(C), ldc, _ptr(amax_out), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))

@@ -325,9 +325,23 @@ size_t moe_permute_noalloc_max_workspace(void) { return nv4::kPermuteStaticBytes
 
 // ---------------------------------------------------------------- grouped GEMM
 
-size_t nvfp4_grouped_gemm_workspace(int group_mode, int E, int64_t M_cap, int64_t N, int64_t K) {
-  (void)E; (void)M_cap; (void)N; (void)K;
-  return group_mode == NV4_GROUP_K ? 256 : 0;  // the dynamic tile schedule's counter
+// Workspace layout of nvfp4_grouped_gemm: [0, 256) the dynamic tile schedule's counter
+// (GROUP_K); then, when K % 64 != 0, A and B repacked to Kp = K rounded up to 64
+// (codes, then scale bytes, each region 256-aligned).
+static int64_t padded_k(int64_t K) { return (K + 63) / 64 * 64; }
+static size_t gemm_ws_bytes(int64_t a_rows, int64_t b_rows, int64_t K, int group_mode) {
+  size_t n = group_mode == NV4_GROUP_K ? 256 : 0;
+  if (K % 64) {
+    const int64_t Kp = padded_k(K);
+    n += round256((size_t)a_rows * (Kp / 2)) + round256((size_t)a_rows * (Kp / 16));
+    n += round256((size_t)b_rows * (Kp / 2)) + round256((size_t)b_rows * (Kp / 16));
+  }
+  return n;
+}
+
+size_t nvfp4_grouped_gemm_workspace(const nv4_tensor *A, const nv4_tensor *B, int group_mode) {
+  if (!A || !B || A->rows < 0 || B->rows < 0 || A->K <= 0) return 0;
+  return gemm_ws_bytes(A->rows, B->rows, A->K, group_mode);
 }
 
 nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const int32_t *offsets, int E,
@@ -343,15 +357,25 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
     return fail(NV4_EINVAL, "nvfp4_grouped_gemm: bad epilogue");
   if (ctype != NV4_BF16 && ctype != NV4_F32) return fail(NV4_EINVAL, "nvfp4_grouped_gemm: bad C dtype");
   if (A->K != B->K) return fail(NV4_EALIGN, "nvfp4_grouped_gemm: A->K != B->K");
-  if (A->K <= 0 || A->K % 64)
-    return fail(NV4_EALIGN, "nvfp4_grouped_gemm: K = %lld must be a positive multiple of 64", (long long)A->K);
+  if (A->K <= 0 || A->K % 16)
+    return fail(NV4_EALIGN, "nvfp4_grouped_gemm: K = %lld must be a positive multiple of 16", (long long)A->K);
   if (!A->codes || !A->scales || !A->tscale || !B->codes || !B->scales || !B->tscale)
     return fail(NV4_EINVAL, "nvfp4_grouped_gemm: NULL tensor buffer");
-  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4))
+  // (K % 64 != 0: both operands are first repacked, zero-padded to a multiple of 64, into the workspace)
+  const bool repack = A->K % 64 != 0;
+  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || (!repack && (!aligned(A->scales, 4) ||
+                                                                       !aligned(B->scales, 4))))
     return fail(NV4_EALIGN, "nvfp4_grouped_gemm: codes must be 16-byte and scales 4-byte aligned");
   // the kernel addresses operands with 32-bit byte offsets and C with 32-bit element offsets
-  if (A->rows < 0 || B->rows < 0 || A->rows * (A->K / 2) >= (1ll << 32) || B->rows * (B->K / 2) >= (1ll << 32))
+  const int64_t Kk = padded_k(A->K);
+  if (A->rows < 0 || B->rows < 0 || A->rows * (Kk / 2) >= (1ll << 32) || B->rows * (Kk / 2) >= (1ll << 32))
     return fail(NV4_EINVAL, "nvfp4_grouped_gemm: each operand must stay below 4 GiB of codes");
+  const size_t need = gemm_ws_bytes(A->rows, B->rows, A->K, group_mode);
+  if (repack && (!ws || ws_bytes < need))
+    return fail(NV4_EWORKSPACE, "nvfp4_grouped_gemm: K = %lld needs a workspace of %zu bytes (repacked operands)",
+                (long long)A->K, need);
+  if (ws && !aligned(ws, 256) && repack)
+    return fail(NV4_EALIGN, "nvfp4_grouped_gemm: workspace must be 256-byte aligned");
   nv4::GemmArgs g{};
   g.a_codes = A->codes;
   g.a_scales = A->scales;
@@ -418,6 +442,27 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
     if ((int64_t)E * A->rows * ldc >= (1ll << 31))
       return fail(NV4_EINVAL, "nvfp4_grouped_gemm: C must stay below 2^31 elements");
     g.N = B->rows;
+  }
+  if (repack) {
+    // zero-padded copies of both operands, then the GEMM on K = Kp (padded blocks carry
+    // scale 0 and add exact zeros)
+    char *p = static_cast<char *>(ws) + (group_mode == NV4_GROUP_K ? 256 : 0);
+    uint8_t *ac = reinterpret_cast<uint8_t *>(p);
+    p += round256((size_t)A->rows * (Kk / 2));
+    uint8_t *as = reinterpret_cast<uint8_t *>(p);
+    p += round256((size_t)A->rows * (Kk / 16));
+    uint8_t *bc = reinterpret_cast<uint8_t *>(p);
+    p += round256((size_t)B->rows * (Kk / 2));
+    uint8_t *bs = reinterpret_cast<uint8_t *>(p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = nv4::launch_repack_k(A->codes, A->scales, A->rows, A->K, ac, as, Kk, st);
+    if (e == hipSuccess) e = nv4::launch_repack_k(B->codes, B->scales, B->rows, B->K, bc, bs, Kk, st);
+    if (e != hipSuccess) return from_hip(e, "nvfp4_grouped_gemm: repack");
+    g.a_codes = ac;
+    g.a_scales = as;
+    g.b_codes = bc;
+    g.b_scales = bs;
+    g.K = Kk;
   }
   return from_hip(nv4::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)), "nvfp4_grouped_gemm");
 }

@@ -611,34 +611,29 @@ void k_gemm(GemmArgs g) {
       if constexpr (S == 2) {
         // pairs of stages with no branch between them, then the odd stage: with a
         // conditional second stage the accumulators were copied between registers
-        // on every iteration.  Stage kt is in buffer kt % 2.
-        int kt = 0;
-        if constexpr (KSPLIT) {
-          const int nks = (int)((K >> 1) / BK);  // stages of the first K half
-          for (; kt + 1 < nks; kt += 2) {
-            stage(0, kt);
-            stage(1, kt + 1);
-          }
-          if (kt < nks) {
-            stage(0, kt);
-            ++kt;
-          }
+        // on every iteration.  Stage kt is in buffer kt % 2.  KSPLIT rescales the
+        // accumulators once, before the first stage of the second K half (a uniform
+        // branch, so that the loop body exists once).
+        const int nks = KSPLIT ? (int)((K >> 1) / BK) : -1;  // first stage of the second K half
+        auto rescale = [&]() {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
               for (int r = 0; r < 16; ++r) acc[i][j][r] *= k_ratio;
-          if (kt & 1) {  // the second half starts in buffer 1
-            stage(1, kt);
-            ++kt;
-          }
-        }
+        };
+        int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
+          if (KSPLIT && kt == nks) rescale();
           stage(0, kt);
+          if (KSPLIT && kt + 1 == nks) rescale();
           stage(1, kt + 1);
         }
-        if (kt < nk) stage(0, kt);
+        if (kt < nk) {
+          if (KSPLIT && kt == nks) rescale();
+          stage(0, kt);
+        }
       } else {
         static_assert(!KSPLIT, "the K-half rescale is built for the two-stage ring");
         for (int kt = 0; kt < nk; kt += S) {

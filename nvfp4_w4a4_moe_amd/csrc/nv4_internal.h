@@ -82,6 +82,10 @@ struct GemmArgs {
   int32_t *tile_counter;         // GROUP_K: workspace word for the dynamic tile schedule, or null
 };
 hipError_t launch_grouped_gemm(const GemmArgs &a, hipStream_t stream);
+// copy an NVFP4 operand [rows][K] (K % 16 == 0) into [rows][Kp] (Kp % 64 == 0, Kp >= K):
+// the extra codes and scale bytes are zero, so the padded blocks add exact zeros
+hipError_t launch_repack_k(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                           uint8_t *codes_p, uint8_t *scales_p, int64_t Kp, hipStream_t stream);
 
 // ---------------------------------------------------------------- BF16 operands
 struct ConvertArgs {

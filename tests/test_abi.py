@@ -133,6 +133,18 @@ def test_gemm_validation(lib):
     bh3 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 768, 1536 + 64, 3, 8)
     assert g(a3, bh3, epi=0) == -3            # K/2 = 800 is not a whole number of 128-wide stages
     assert b"K/2" in lib.nv4_last_error()
+    # K % 16 is the contract; K % 64 != 0 needs the workspace for the repacked operands
+    a40 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 40, 0, 1)
+    b40 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 40, 1, 8)
+    assert g(a40, b40) == -2
+    a80 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 256, 80, 0, 1)
+    b80 = nv4.NV4Tensor(0x1000, 0x1000, 0x1000, 8 * 1536, 80, 1, 8)
+    assert g(a80, b80) == -4 and b"workspace" in lib.nv4_last_error()
+    need = lib.nvfp4_grouped_gemm_workspace(ctypes.byref(a80), ctypes.byref(b80), 0)
+    pad = lambda n: (n + 255) // 256 * 256
+    assert need == pad(256 * 64) + pad(256 * 8) + pad(8 * 1536 * 64) + pad(8 * 1536 * 8)
+    assert lib.nvfp4_grouped_gemm_workspace(ctypes.byref(a), ctypes.byref(b), 0) == 0
+    assert lib.nvfp4_grouped_gemm_workspace(ctypes.byref(a), ctypes.byref(b), 1) == 256
 
 
 def test_combine_validation(lib):

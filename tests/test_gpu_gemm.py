@@ -268,3 +268,40 @@ def test_per_half_scales_need_whole_stages(gpu_lib):
     with pytest.raises(gpu_lib.NV4Error) as ei:
         gpu_lib.nvfp4_grouped_gemm(dyq, wt.w13t, off, E, H, M_cap=64)
     assert "NV4_EUNSUPPORTED" in str(ei.value) or "NV4_EALIGN" in str(ei.value)
+
+
+@pytest.mark.parametrize("K", [16, 48, 80, 208])
+def test_k_multiple_of_16(gpu_lib, K):
+    """The format's only constraint on K is whole 16-element blocks ("The 4-bitter
+    Lesson", "Baseline": blocks of 16).  K % 64 != 0 runs through the workspace copy
+    zero-padded to 64: GROUP_M (with a ragged and an empty expert, the SwiGLU epilogue
+    and the fused gather) and GROUP_K (ragged 16-aligned contraction ranges), each
+    within 1e-5 of the oracle, bitwise repeatable."""
+    E = 4
+    counts = np.array([37, 0, 130, 9])
+    R = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    for epi, N in ((0, 96), (1, 64)):
+        nb = 2 * N if epi else N
+        a = synth.activations(R, K, 70 + K)
+        b = synth.weights((E * nb, K), 71 + K)
+        aq = gpu_lib.nvfp4_quantize(dev_bf16(a))
+        bq = gpu_lib.nvfp4_quantize(dev_bf16(b), scale_mode=gpu_lib.NV4_SCALE_SEGMENT, nseg=E)
+        perm = synth.rng(K).permutation(R).astype(np.int32)
+        C = gpu_lib.nvfp4_grouped_gemm(aq, bq, dev_i32(off), E, N, M_cap=R, a_rows=dev_i32(perm), epilogue=epi)
+        A_h = nvfp4_host(aq).dequant()[perm]
+        raw = moe.grouped_gemm_m(A_h, nvfp4_host(bq).dequant(), off, E, nb)
+        ref = moe.swiglu(raw) if epi else raw
+        assert rel_frob(host(C), ref) <= TOL
+        C2 = gpu_lib.nvfp4_grouped_gemm(aq, bq, dev_i32(off), E, N, M_cap=R, a_rows=dev_i32(perm), epilogue=epi)
+        assert torch.equal(C.view(torch.int32), C2.view(torch.int32))
+    # GROUP_K: A [N][Kcap], B [M][Kcap] with 16-aligned expert ranges inside Kcap = K
+    Kc = K
+    ko = np.array([0, min(16, Kc), min(16, Kc), Kc, Kc]).astype(np.int32)
+    a = synth.activations(72, Kc, 80 + K)
+    b = synth.activations(40, Kc, 81 + K)
+    aq, bq = gpu_lib.nvfp4_quantize(dev_bf16(a)), gpu_lib.nvfp4_quantize(dev_bf16(b))
+    Cg = gpu_lib.nvfp4_grouped_gemm(aq, bq, dev_i32(ko), E, 72, group_mode=gpu_lib.NV4_GROUP_K)
+    ref = moe.grouped_gemm_k(nvfp4_host(aq).dequant(), nvfp4_host(bq).dequant(), ko, E)
+    assert rel_frob(host(Cg), ref) <= TOL
+    assert not host(Cg)[1].any() and not host(Cg)[3].any()     # empty ranges give zeros
