@@ -1,8 +1,8 @@
 // Grouped NVFP4 x NVFP4 GEMM for gfx950: dispatch to the kernel instantiation for
 // the operand type, group mode, epilogue and A-scale mode.  The kernel is in
 // gemm_kernel.h; its instantiations are compiled in gemm_m.hip, gemm_m_rows.hip,
-// gemm_m_swiglu.hip, gemm_m_swiglu_rows.hip, gemm_m_ksplit.hip, gemm_k.hip and
-// gemm_bf16.hip.
+// gemm_m_swiglu.hip, gemm_m_swiglu_rows.hip, gemm_m_ksplit.hip, gemm_m_small.hip,
+// gemm_k.hip and gemm_bf16.hip.
 #include <algorithm>
 
 #include "nv4_internal.h"
@@ -17,6 +17,7 @@ hipError_t launch_gemm_m_swiglu_rows(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_k(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_m_ksplit(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_m_small(const GemmArgs &g, hipStream_t stream);
 
 namespace {
 
@@ -59,7 +60,13 @@ hipError_t launch_grouped_gemm(const GemmArgs &g, hipStream_t stream) {
   if (g.group_mode == NV4_GROUP_K) return launch_gemm_k(g, stream);
   if (g.b_scale_mode == NV4_SCALE_SEGMENT_HALVES) return launch_gemm_m_ksplit(g, stream);
   if (g.epilogue == NV4_EPI_SWIGLU) return rows ? launch_gemm_m_swiglu_rows(g, stream) : launch_gemm_m_swiglu(g, stream);
-  return rows ? launch_gemm_m_rows(g, stream) : launch_gemm_m(g, stream);
+  if (rows) return launch_gemm_m_rows(g, stream);
+  // Upper estimate of the 256 x 256 tiles (every expert adds at most one partial M
+  // tile; the row counts stay on the device): with fewer than two per compute unit,
+  // the 128 x 256 tiles spread the work over twice as many workgroups.
+  const int64_t tiles = ((g.M_cap + 255) / 256 + g.E) * ((g.N + 255) / 256);
+  if (tiles < 2 * (int64_t)device_cu_count()) return launch_gemm_m_small(g, stream);
+  return launch_gemm_m(g, stream);
 }
 
 }  // namespace nv4

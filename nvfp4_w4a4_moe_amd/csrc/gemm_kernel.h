@@ -744,6 +744,10 @@ void k_gemm(GemmArgs g) {
 // 5-19 % faster than with 256 x 128 tiles of four waves, two workgroups per CU.)
 using GemmTile = TileCfg<2, 4, 4, 2, 2, 2>;
 using GemmTileK = GemmTile;
+// Problems with few 256 x 256 tiles (a single dense GEMM of 8192 x 768 outputs has 96 of
+// them for 256 compute units): 128 x 256 workgroup tiles of eight 64 x 64 wave tiles,
+// twice the tiles at 8 instead of 6 decode instructions per MFMA.
+using GemmTileSmall = TileCfg<2, 4, 2, 2, 2, 2>;
 // BF16 operands: 128 x 256 workgroup tiles of four 64 x 128 wave tiles, two
 // workgroups per CU, double-buffered 24 KB stages.  (Measured on the learner
 // batch: 15-25 % faster than 256 x 256 tiles with one workgroup per CU, whether
