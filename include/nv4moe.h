@@ -226,6 +226,19 @@ nv4_status nvfp4_quantize_sr(const void *x, nv4_dtype xtype, int64_t rows, int64
                              void *ws, size_t ws_bytes, int32_t *dev_status, uint64_t seed, void *stream);
 
 /*
+ * nv4_amax -- *amax = max_i |x[i]| over n FP32 values (0 when n == 0).  [4BL] "Why is
+ * the NVFP4 pretraining recipe not sufficient for RL?": with per-token scales the
+ * quantiser records each row's amax (amax_out of nvfp4_quantize with NV4_SCALE_ROW);
+ * their maximum is the tensor amax, so a per-tensor quantisation of the same tensor
+ * (the token-direction operand of a weight gradient) takes it through amax_in without
+ * another pass over the tensor.
+ *   x      device FP32 [n];  amax  device FP32 [1], overwritten;
+ *   dev_status  optional device word: NV4_DS_NONFINITE for a NaN or infinity.
+ * Errors: EINVAL (n < 0, NULL pointers), EHIP.
+ */
+nv4_status nv4_amax(const float *x, int64_t n, float *amax, int32_t *dev_status, void *stream);
+
+/*
  * moe_permute -- route tokens to experts and permute them by expert.
  * [LBP] "What W4A4 GEMM Actually Changes" (expert routing concentrates
  * activations); [MTE] "Background: Same Weights Did Not Guarantee Same Policy"

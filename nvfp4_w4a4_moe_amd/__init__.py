@@ -68,6 +68,7 @@ _SIGS = {
                             ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
     "nvfp4_quantize_sr": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                                ctypes.POINTER(NV4Tensor), _P, _SZ, _P, ctypes.c_uint64, _P]),
+    "nv4_amax": (_I, [_P, _I64, _P, _P, _P]),
     "moe_permute_workspace": (_SZ, [_I64, _I, _I]),
     "moe_permute": (_I, [_P, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, ctypes.POINTER(NV4Tensor),
                          ctypes.POINTER(NV4Tensor), _P, _SZ, _P, _P]),
@@ -207,6 +208,17 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
         out_rows.scale_mode, out_rows.nseg = d2.scale_mode, d2.nseg
         out.rows_out = out_rows
     return out
+
+
+def nv4_amax(x: torch.Tensor, amax: torch.Tensor | None = None, dev_status: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """max |x| of an FP32 tensor into a one-element FP32 tensor (e.g. the tensor amax
+    from the per-row amaxes a per-token quantisation recorded)."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(load().nv4_amax(_ptr(x), x.numel(), _ptr(amax), _ptr(dev_status), _stream(stream)))
+    return amax
 
 
 @dataclass
@@ -513,7 +525,6 @@ class BackwardBuffers:
     dw2: torch.Tensor       # [E, H, I]
     dw13: torch.Tensor      # [E, 2I, H]
     x_amax: torch.Tensor | None = None  # tensor amax of X when the forward scaled per token
-    x_tq: NVFP4 | None = None            # (its by-product: X quantised with one tensor scale)
     gemm_ws: torch.Tensor | None = None  # the weight-gradient GEMMs' tile-schedule workspace
 
 
@@ -594,12 +605,8 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
             nvfp4_quantize(dY13, amax_in=bufs.dy13_amax, out=bufs.dy13c, sr_seed=sr13, **seg)
     with _Stage(stage_events, "quantize_cols_x", st):
         if fwd.token_scale:
-            # the forward kept per-token amaxes: the tensor's comes from one quantisation
-            # pass over X itself (T rows) rather than an amax pass over the k-times
-            # gathered rows
-            if bufs.x_tq is None or bufs.x_tq.rows != T:
-                bufs.x_tq = NVFP4.empty(T, H, 1, device=x.device)
-            nvfp4_quantize(x, out=bufs.x_tq, amax_out=bufs.x_amax, stream=stream)
+            # the forward recorded every token's amax: their maximum is the tensor amax
+            nv4_amax(fwd.xamax, bufs.x_amax, stream=stream)
             nvfp4_quantize(x, amax_in=bufs.x_amax, out=bufs.xc, row_index=rt.row_token, **seg)
         else:
             nvfp4_quantize(x, amax_in=fwd.xamax, out=bufs.xc, row_index=rt.row_token, **seg)

@@ -232,6 +232,11 @@ nv4_status nvfp4_quantize_sr(const void *x, nv4_dtype xtype, int64_t rows, int64
                        seed);
 }
 
+nv4_status nv4_amax(const float *x, int64_t n, float *amax, int32_t *dev_status, void *stream) {
+  if (n < 0 || !amax || (n > 0 && !x)) return fail(NV4_EINVAL, "nv4_amax: bad arguments");
+  return from_hip(nv4::launch_amax_vec(x, n, amax, dev_status, static_cast<hipStream_t>(stream)), "nv4_amax");
+}
+
 // ---------------------------------------------------------------- routing / permutation
 
 size_t moe_permute_workspace(int64_t T, int E, int k) {

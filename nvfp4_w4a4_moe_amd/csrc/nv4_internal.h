@@ -33,6 +33,7 @@ struct QuantArgs {
   uint64_t sr_seed;
 };
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream);
+hipError_t launch_amax_vec(const float *x, int64_t n, float *amax, int32_t *dev_status, hipStream_t stream);
 
 // ---------------------------------------------------------------- routing / permutation
 constexpr int kPermuteChunk = 1024;  // assignments ranked per wave

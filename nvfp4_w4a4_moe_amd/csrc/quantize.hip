@@ -378,50 +378,120 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantArgs a) {
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
 }
 
-// Row layout with one scale per row (the per-token variant): one wave per row,
-// amax and quantisation fused (the row is read twice, the second time from cache).
-template <bool F32, bool SR>
+// Row layout with one scale per row (the per-token variant): one wave per row, amax
+// and quantisation fused.  Rows of up to NC * 512 elements stay in registers between
+// the row-amax reduction and the quantisation (one read of x), and the next row's
+// loads are in flight while the current row is quantised.  NC = 0: longer rows, read
+// twice (the second time from cache).
+template <bool F32, bool SR, int NC>
 __global__ __launch_bounds__(kThreads) void k_quant_rows_per_row(QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
   bool bad = false;
-  for (int64_t row = wave; row < a.rows; row += nwaves) {
-    const int64_t base = row_off(a, row);
-    float A;
-    if (a.amax_in) {
-      A = a.amax_in[row];
-    } else {
-      float m = 0.0f;
-      for (int64_t k = (int64_t)lane * 8; k < a.K; k += 512) {
-        float v[8];
-        unpack_chunk<F32>(load_chunk<F32>(a.x, base + k), v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-      }
-      A = wave_max(m);
+  auto store = [&](int64_t row, int64_t k, uint32_t p, uint32_t sf) {
+    if (k < a.K) {
+      reinterpret_cast<uint32_t *>(a.codes)[row * (a.out_K >> 3) + (k >> 3)] = p;
+      if (((k >> 3) & 1) == 0) a.scales[row * (a.out_K >> 4) + (k >> 4)] = (uint8_t)sf;
     }
+  };
+  auto finish_scale = [&](int64_t row, float A) {
     const float S = tensor_encode_scale(A);
     if (lane == 0) {
       a.tscale[row] = __fdiv_rn(1.0f, S);
       if (a.amax_acc) a.amax_acc[row] = A;
     }
-    for (int64_t k0 = 0; k0 < a.K; k0 += 512) {
-      const int64_t k = k0 + (int64_t)lane * 8;
-      const bool act = k < a.K;
-      float v[8];
-      unpack_chunk<F32>(load_chunk<F32>(a.x, base + (act ? k : k0)), v);
-      uint32_t sf;
-      Rand4 rnd;
-      if (SR) rnd = philox4x64_10((uint64_t)(k >> 3), (uint64_t)row, 0, 0, a.sr_seed);
-      const uint32_t p = quant_half_block<SR>(v, S, nullptr, sf, bad, &rnd);
-      if (act) {
-        reinterpret_cast<uint32_t *>(a.codes)[row * (a.out_K >> 3) + (k >> 3)] = p;
-        if (((k >> 3) & 1) == 0) a.scales[row * (a.out_K >> 4) + (k >> 4)] = (uint8_t)sf;
+    return S;
+  };
+  if constexpr (NC > 0) {
+    const int nc = (int)((a.K + 511) >> 9);  // 512-element rounds of the wave per row (<= NC)
+    auto load_row = [&](int64_t row, Chunk<F32> (&c)[NC]) {
+      const int64_t base = row_off(a, row < a.rows ? row : 0);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int64_t k = (int64_t)i * 512 + lane * 8;
+        if (i < nc) c[i] = load_chunk<F32>(a.x, base + (k < a.K ? k : (int64_t)i * 512));
+      }
+    };
+    Chunk<F32> cur[NC], nxt[NC];
+    if (wave < a.rows) load_row(wave, cur);
+    for (int64_t row = wave; row < a.rows; row += nwaves) {
+      if (row + nwaves < a.rows) load_row(row + nwaves, nxt);
+      float A;
+      if (a.amax_in) {
+        A = a.amax_in[row];
+      } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          if (i < nc && (int64_t)i * 512 + lane * 8 < a.K) {
+            float v[8];
+            unpack_chunk<F32>(cur[i], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+          }
+        }
+        A = wave_max(m);
+      }
+      const float S = finish_scale(row, A);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        if (i < nc) {
+          const int64_t k = (int64_t)i * 512 + lane * 8;
+          float v[8];
+          unpack_chunk<F32>(cur[i], v);
+          uint32_t sf;
+          Rand4 rnd;
+          if (SR) rnd = philox4x64_10((uint64_t)(k >> 3), (uint64_t)row, 0, 0, a.sr_seed);
+          store(row, k, quant_half_block<SR>(v, S, nullptr, sf, bad, &rnd), sf);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NC; ++i) cur[i] = nxt[i];
+    }
+  } else {
+    for (int64_t row = wave; row < a.rows; row += nwaves) {
+      const int64_t base = row_off(a, row);
+      float A;
+      if (a.amax_in) {
+        A = a.amax_in[row];
+      } else {
+        float m = 0.0f;
+        for (int64_t k = (int64_t)lane * 8; k < a.K; k += 512) {
+          float v[8];
+          unpack_chunk<F32>(load_chunk<F32>(a.x, base + k), v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        }
+        A = wave_max(m);
+      }
+      const float S = finish_scale(row, A);
+      for (int64_t k0 = 0; k0 < a.K; k0 += 512) {
+        const int64_t k = k0 + (int64_t)lane * 8;
+        float v[8];
+        unpack_chunk<F32>(load_chunk<F32>(a.x, base + (k < a.K ? k : k0)), v);
+        uint32_t sf;
+        Rand4 rnd;
+        if (SR) rnd = philox4x64_10((uint64_t)(k >> 3), (uint64_t)row, 0, 0, a.sr_seed);
+        store(row, k, quant_half_block<SR>(v, S, nullptr, sf, bad, &rnd), sf);
       }
     }
   }
   if (bad && a.dev_status) atomicOr(a.dev_status, kDsNonFinite);
+}
+
+// A = max |x[i]| over n FP32 values (the tensor amax from recorded per-row amaxes)
+__global__ __launch_bounds__(kThreads) void k_amax_vec(const float *x, int64_t n, float *amax, int32_t *dev_status) {
+  float m = 0.0f;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const float v = fabsf(x[i]);
+    bad |= !(v <= 3.402823466e38f);
+    m = fmaxf(m, v);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  if (bad && dev_status) atomicOr(dev_status, kDsNonFinite);
 }
 
 // Column layouts (transposed operands of the backward GEMMs).  Output row `c`
@@ -697,8 +767,17 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
   if (a.layout == NV4_ROWS) {
     if (per_row) {
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((a.rows + 3) / 4, (int64_t)cus * 16));
-      if (f32) k_quant_rows_per_row<true, SR><<<grid, kThreads, 0, stream>>>(a);
-      else k_quant_rows_per_row<false, SR><<<grid, kThreads, 0, stream>>>(a);
+      // register cache of 2, 4 or 8 rounds of 512 elements, or none for longer rows
+      const int64_t nc = (a.K + 511) / 512;
+      auto go = [&](auto ncc) {
+        constexpr int N = decltype(ncc)::value;
+        if (f32) k_quant_rows_per_row<true, SR, N><<<grid, kThreads, 0, stream>>>(a);
+        else k_quant_rows_per_row<false, SR, N><<<grid, kThreads, 0, stream>>>(a);
+      };
+      if (nc <= 2) go(std::integral_constant<int, 2>{});
+      else if (nc <= 4) go(std::integral_constant<int, 4>{});
+      else if (nc <= 8) go(std::integral_constant<int, 8>{});
+      else go(std::integral_constant<int, 0>{});
     } else {
       const int64_t chunks = a.rows * (a.K >> 3);
       const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + 2 * kThreads - 1) / (2 * kThreads), (int64_t)cus * 8));
@@ -745,6 +824,15 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_amax_vec(const float *x, int64_t n, float *amax, int32_t *dev_status, hipStream_t stream) {
+  k_fill_zero<<<1, 64, 0, stream>>>(amax, 1);
+  if (n > 0) {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 256));
+    k_amax_vec<<<grid, kThreads, 0, stream>>>(x, n, amax, dev_status);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t stream) {
   return a.sr ? launch_quantize_t<true>(a, stream) : launch_quantize_t<false>(a, stream);

@@ -324,3 +324,32 @@ def test_columns_with_segment_scales_exact(gpu_lib):
     assert np.array_equal(host(t.scales)[:, : Kp // 16], ref.scales)
     assert np.array_equal(host(t.tscale).view(np.uint32), ref.G.view(np.uint32))
     assert len(set(ref.G.tolist())) >= 3
+
+
+@pytest.mark.parametrize("K,f32", [(4096, False), (4608, False), (784, True), (8192 + 16, True)])
+def test_rows_per_token_long_and_fp32_rows(gpu_lib, K, f32):
+    """NV4_SCALE_ROW with rows held in registers (K <= 4096) and rows read twice
+    (longer), BF16 and FP32 input: bit-exact, per-row amaxes exact."""
+    x = synth.activations(37, K, 90 + K)
+    amax = torch.empty(37, dtype=torch.float32, device="cuda")
+    t = gpu_lib.nvfp4_quantize(dev_f32(x) if f32 else dev_bf16(x), scale_mode=gpu_lib.NV4_SCALE_ROW, amax_out=amax)
+    _assert_exact(t, Q.quantize_rows(x, "row"))
+    assert np.array_equal(host(amax), np.abs(x).max(axis=1))
+
+
+def test_amax_of_recorded_row_amaxes(gpu_lib):
+    """nv4_amax: the tensor amax from the per-row amaxes equals max |x| over the tensor,
+    so the per-tensor column quantisation of a per-token-scaled tensor needs no extra
+    pass; a NaN sets the status bit; n = 0 gives 0."""
+    x = synth.activations(3001, 64, 95)
+    rows = torch.empty(3001, dtype=torch.float32, device="cuda")
+    gpu_lib.nvfp4_quantize(dev_bf16(x), scale_mode=gpu_lib.NV4_SCALE_ROW, amax_out=rows)
+    A = gpu_lib.nv4_amax(rows)
+    assert host(A)[0] == np.abs(x).max()
+    z = gpu_lib.nv4_amax(torch.empty(0, dtype=torch.float32, device="cuda"))
+    assert host(z)[0] == 0.0
+    bad = torch.ones(100, dtype=torch.float32, device="cuda")
+    bad[17] = float("nan")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpu_lib.nv4_amax(bad, dev_status=st)
+    assert int(st.item()) & gpu_lib.NV4_DS_NONFINITE
