@@ -243,6 +243,13 @@ def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
     r["gbs"] = round(2 * n / (r["median_ms"] * 1e-3) / 1e9, 1)
     r["kernel"] = "k_stream_read"
     res["read"] = r
+    quarter = torch.empty(2 * n // 16, dtype=torch.float32, device="cuda")
+    nv4.nv4_bench_mix(big, quarter)
+    m = stats(timed_events(torch, lambda: nv4.nv4_bench_mix(big, quarter), reps, st))
+    m["gbs"] = round(2.5 * n / (m["median_ms"] * 1e-3) / 1e9, 1)
+    m["kernel"] = "k_stream_mix (4 B read : 1 B written)"
+    res["mix_4_1"] = m
+    del quarter
     del src, dst, big
     out = None
     for w in (1, 2):
@@ -497,6 +504,7 @@ def summarize(cfg, res, part, recipe, ceil) -> dict:
     mfma_ceil = ceil.get("mfma_f16_2wave", {}).get("tflops") if ceil else None
     read_ceil = ceil.get("read", {}).get("gbs") if ceil else None
     copy_ceil = ceil.get("copy", {}).get("gbs") if ceil else None
+    mix_ceil = ceil.get("mix_4_1", {}).get("gbs") if ceil else None
     other = {}
     for n, (tf, desc) in gemm.items():
         e = {"achieved_tflops": round(tf, 2), "frac": round(tf / PEAK_F16_MFMA_TFLOPS, 4),
@@ -512,6 +520,7 @@ def summarize(cfg, res, part, recipe, ceil) -> dict:
             if read_ceil:
                 e["frac_of_measured_read_stream"] = round(gbs / read_ceil, 4)
                 e["frac_of_measured_copy_stream"] = round(gbs / copy_ceil, 4)
+                e["frac_of_measured_4to1_stream"] = round(gbs / mix_ceil, 4)
             other[n] = e
     t_med = res["flushed"]["median_ms"]
     out = {"ms_per_step": round(res["ms_per_step"], 4), "flushed": res["flushed"],

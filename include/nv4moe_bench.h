@@ -34,6 +34,11 @@ nv4_status nv4_bench_copy(const void *src, void *dst, size_t bytes, void *stream
  * caller that passes a value the data cannot produce gets a pure read stream. */
 nv4_status nv4_bench_read(const void *src, size_t bytes, uint32_t never, uint32_t *sink, void *stream);
 
+/* Read `bytes` (a positive multiple of 4096) of src and write bytes / 4 to dst, a
+ * quantiser's 4:1 read:write mix (BF16 in, FP4 codes out), with 16-byte non-temporal
+ * loads and stores: 1.25 * bytes of HBM traffic. */
+nv4_status nv4_bench_mix(const void *src, size_t bytes, void *dst, void *stream);
+
 /* A loop of `iters` x 8 independent v_mfma_f32_32x32x16_f16 per wave (32768 FLOP
  * each), with waves_per_simd (1 or 2) waves on every SIMD of every compute unit
  * and no memory traffic in the loop.  `out` receives one float per lane:

@@ -86,6 +86,7 @@ _SIGS = {
     # measurement kernels (include/nv4moe_bench.h)
     "nv4_bench_copy": (_I, [_P, _P, _SZ, _P]),
     "nv4_bench_read": (_I, [_P, _SZ, ctypes.c_uint32, _P, _P]),
+    "nv4_bench_mix": (_I, [_P, _SZ, _P, _P]),
     "nv4_bench_mfma_out_floats": (_SZ, [_I]),
     "nv4_bench_mfma": (_I, [_P, _I, _I, _P]),
 }
@@ -835,6 +836,13 @@ def nv4_bench_read(src: torch.Tensor, sink: torch.Tensor, never: int = 0xDEADBEE
     """Stream-read src (a pure read stream unless the XOR of its words equals `never`)."""
     _check(load().nv4_bench_read(_ptr(src), src.numel() * src.element_size(), ctypes.c_uint32(never), _ptr(sink),
                                  _stream(stream)))
+
+
+def nv4_bench_mix(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Read all of src and write a quarter of its bytes to dst (a quantiser's traffic mix)."""
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nb // 4
+    _check(load().nv4_bench_mix(_ptr(src), nb, _ptr(dst), _stream(stream)))
 
 
 def nv4_bench_mfma(out: torch.Tensor | None, iters: int, waves_per_simd: int = 2, stream=None) -> tuple:

@@ -10,6 +10,7 @@
 //   k_stream_read  the same loads only; the XOR of the data goes to a sink word only
 //                  when it equals a value the caller never passes, so nothing is
 //                  written in practice and the loads cannot be removed.
+//   k_stream_mix   4 reads of 16 bytes per 16-byte write, a quantiser's read:write mix.
 //   k_mfma_loop    eight independent v_mfma_f32_32x32x16_f16 chains per wave with no
 //                  memory traffic: the matrix-core issue rate at a given occupancy.
 #include <hip/hip_runtime.h>
@@ -56,6 +57,23 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const u32x4 *__r
   for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == never) sink[0] = x;
+}
+
+// Reads 4 x 16 bytes and writes 16 bytes per lane per round: the 4:1 read:write mix of
+// a quantiser (2 bytes in, 0.5 bytes of codes and 1/16 byte of scales out per element).
+// dst holds n / 4 vectors.
+__global__ __launch_bounds__(kStreamThreads) void k_stream_mix(const u32x4 *__restrict__ src,
+                                                               u32x4 *__restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  // n % 256 == 0, so every j + 192 below stays under n
+  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n / 4; i += stride) {
+    const int64_t j = (i / 64) * 256 + (i % 64);   // a wave reads 4 consecutive 1 KB runs
+    u32x4 v = __builtin_nontemporal_load(src + j);
+    v ^= __builtin_nontemporal_load(src + j + 64);
+    v ^= __builtin_nontemporal_load(src + j + 128);
+    v ^= __builtin_nontemporal_load(src + j + 192);
+    __builtin_nontemporal_store(v, dst + i);
+  }
 }
 
 // Eight accumulator chains of 32x32x16 FP16 MFMAs per wave.  The operands depend on
@@ -117,6 +135,17 @@ nv4_status nv4_bench_read(const void *src, size_t bytes, uint32_t never, uint32_
   const int64_t n = (int64_t)(bytes / 16);
   nv4::k_stream_read<<<nv4::stream_grid(n), nv4::kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const nv4::u32x4 *>(src), n, never, sink);
+  return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
+}
+
+nv4_status nv4_bench_mix(const void *src, size_t bytes, void *dst, void *stream) {
+  if (!src || !dst || bytes == 0 || bytes % 4096) return NV4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16) return NV4_EALIGN;
+  const int64_t n = (int64_t)(bytes / 16);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n / 4 + nv4::kStreamThreads - 1) / nv4::kStreamThreads,
+                                                               (int64_t)nv4::device_cu_count() * 16));
+  nv4::k_stream_mix<<<grid, nv4::kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const nv4::u32x4 *>(src), static_cast<nv4::u32x4 *>(dst), n);
   return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
 }
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "nvfp4_quantize", "moe_permute_workspace", "moe_permute",
                           "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
                           "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr",
-                          "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma",
+                          "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma", "nv4_bench_mix",
                           "moe_permute_noalloc", "moe_permute_noalloc_max_workspace", "nv4_amax"}
 
 
