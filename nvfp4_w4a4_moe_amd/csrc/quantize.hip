@@ -511,6 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_vec(const float *x, int64_t n
 // With ROWS_TOO (NV4_ROWS_AND_COLS) the same tile also yields the row-direction
 // quantisation of its rows (blocks of 16 columns), so the source is read once for
 // both operands of a tensor that feeds a data gradient and a weight gradient.
+constexpr int kSegLds = 256;       // segment offsets staged in LDS up to this many segments
 constexpr int kOutPitch = 72;       // LDS out-tile row pitch for 64 code bytes (+8 breaks bank aliasing)
 constexpr int kScalePitch = 12;
 
@@ -540,6 +541,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   __shared__ int64_t bsrc[NB];
   __shared__ int bnum[NB], bgrp[NB];
   __shared__ float inv_tab[128];
+  __shared__ int seg_pad[kSegLds + 1], seg_off[kSegLds + 1];
 
   if (blockIdx.x == 0 && blockIdx.y == 0) write_group_scales(a);
   const float *A = amax_src(a);
@@ -559,6 +561,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     orow0 = c0;
   }
   if (p0 >= plimit) return;  // uniform over the workgroup
+  // NV4_COLS: the segments' offsets, searched below, from LDS when they fit (one
+  // coalesced load instead of a chain of dependent loads)
+  const bool seg_in_lds = !batched && a.nseg <= kSegLds;
+  if (seg_in_lds) {
+    for (int i = threadIdx.x; i <= a.nseg; i += kThreads) {
+      seg_pad[i] = a.seg_padded_offsets[i];
+      seg_off[i] = a.seg_offsets[i];
+    }
+    __syncthreads();
+  }
   // SCALE_SEGMENT_HALVES (batched only): positions [0, m/2) of matrix s take group
   // 2s, [m/2, m) group 2s + 1 (the first and second half of the matrix's rows)
   const bool halves = a.scale_mode == NV4_SCALE_SEGMENT_HALVES;
@@ -575,13 +587,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
         n = 16;
         g = halves ? 2 * s_tile + (p >= plimit / 2 ? 1 : 0) : (seg_scales ? s_tile : 0);
       } else {
+        const int *pad = seg_in_lds ? seg_pad : a.seg_padded_offsets;
+        const int *off = seg_in_lds ? seg_off : a.seg_offsets;
         int lo = 0, hi = a.nseg - 1;  // last segment s with pad[s] <= p
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (a.seg_padded_offsets[mid] <= p) lo = mid; else hi = mid - 1;
+          if (pad[mid] <= p) lo = mid; else hi = mid - 1;
         }
-        start = a.seg_offsets[lo] + (p - a.seg_padded_offsets[lo]);
-        n = (int)std::min<int64_t>(16, std::max<int64_t>(0, a.seg_offsets[lo + 1] - start));
+        start = off[lo] + (p - pad[lo]);
+        n = (int)std::min<int64_t>(16, std::max<int64_t>(0, off[lo + 1] - start));
         g = seg_scales ? lo : 0;
       }
     }
