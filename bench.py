@@ -58,9 +58,10 @@ GEMMS = {
 }
 
 
-def hbm_bytes(cfg, recipe: str = "nvfp4") -> dict:
+def hbm_bytes(cfg, recipe: str = "nvfp4", hact_cols: bool = False) -> dict:
     """Algorithmic HBM bytes of the memory-bound kernels (NVFP4: 0.5 B per code and
-    1/16 B per scale; BF16 2 B, FP32 4 B)."""
+    1/16 B per scale; BF16 2 B, FP32 4 B).  hact_cols: the forward's SwiGLU-output
+    quantisation also writes the column form."""
     T, H, I, k, R, E = cfg.T, cfg.H, cfg.I, cfg.k, cfg.R, cfg.E
     q1 = 2 + 0.5 + 1 / 16           # one-pass quantiser, per element
     kc = ((R + 15 * E + 63) // 64) * 64
@@ -69,7 +70,7 @@ def hbm_bytes(cfg, recipe: str = "nvfp4") -> dict:
     dual = lambda C: R * C * (2 + 2 + 0.5 + 1 / 16) + C * kc * (0.5 + 1 / 16)
     return {
         "quantize_x": T * H * (2 + q1),                      # amax pass + one pass
-        "quantize_hact": R * I * q1,
+        "quantize_hact": R * I * q1 + (I * kc * (0.5 + 1 / 16) if hact_cols else 0),
         "combine": T * (k * H * 4 + k * 8 + H * 2),
         "quantize_dy2": dual(H),
         "quantize_dy13": dual(2 * I),
@@ -340,7 +341,10 @@ def time_recipe(nv4, torch, np, cfg, inp, recipe, part, args, stages: bool, flus
         wq_ms.append(e0.elapsed_time(e1))
 
     if nvfp4_fwd:
-        fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, token_scale=args.token_scale)
+        # a full step quantises the SwiGLU output once for its rows and columns (the
+        # column form is the NVFP4 backward's); a timed backward alone does its own
+        hact_cols = part == "fwd+bwd" and recipe in ("nvfp4", "nvfp4-sr") and not args.token_scale
+        fb = nv4.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, token_scale=args.token_scale, hact_cols=hact_cols)
     else:
         fb = nv4.alloc_forward_bf16(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I)
     bb = None
@@ -500,7 +504,9 @@ def summarize(cfg, res, part, recipe, ceil) -> dict:
     med = {k: v["median_ms"] for k, v in res["stages"].items()}
     gemm = {n: (m * rhi / (med[n] * 1e-3) / 1e12, desc) for n, (m, desc) in GEMMS.items() if n in med}
     dom = max(gemm, key=lambda n: med[n]) if gemm else None
-    nbytes = hbm_bytes(cfg, recipe)
+    # the forward made the SwiGLU output's column form when the step's backward did not
+    hact_cols = part == "fwd+bwd" and recipe in ("nvfp4", "nvfp4-sr") and "quantize_cols_hact" not in med
+    nbytes = hbm_bytes(cfg, recipe, hact_cols)
     mfma_ceil = ceil.get("mfma_f16_2wave", {}).get("tflops") if ceil else None
     read_ceil = ceil.get("read", {}).get("gbs") if ceil else None
     copy_ceil = ceil.get("copy", {}).get("gbs") if ceil else None

@@ -389,15 +389,22 @@ class ForwardBuffers:
     routing: Routing | None = None
     token_scale: bool = False   # per-token FP32 scales for X and the SwiGLU output
     hamax_rows: torch.Tensor | None = None  # per-row amax of the SwiGLU output (per-token mode)
+    hc: NVFP4 | None = None     # [I, Kcap] the SwiGLU output's column form, filled with hq when allocated
 
 
 def alloc_forward(T: int, H: int, E: int, k: int, I: int, out_dtype=torch.bfloat16, hact_dtype=torch.bfloat16,
-                  device="cuda", token_scale: bool = False) -> ForwardBuffers:
+                  device="cuda", token_scale: bool = False, hact_cols: bool = False) -> ForwardBuffers:
     """token_scale: X and the SwiGLU output carry one FP32 scale per row (the
-    per-token recipe) instead of one per tensor."""
+    per-token recipe) instead of one per tensor.  hact_cols (a backward follows;
+    tensor scales, BF16 SwiGLU output, I % 64 == 0): the forward also produces the
+    SwiGLU output's column (token-direction) quantisation, reading it once for both
+    its row and its column form; moe_backward then takes it from here."""
     lib = load()
     R = T * k
+    if hact_cols and (token_scale or hact_dtype != torch.bfloat16 or I % 64):
+        raise ValueError("hact_cols needs tensor scales, a BF16 SwiGLU output and I % 64 == 0")
     return ForwardBuffers(
+        hc=NVFP4.empty(I, cols_capacity(R, E), 1, device) if hact_cols else None,
         xq=NVFP4.empty(T, H, T if token_scale else 1, device),
         xamax=torch.zeros((T if token_scale else 1,), dtype=torch.float32, device=device),
         xg=NVFP4.empty(R, H, 1, device),
@@ -473,6 +480,11 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights, k: int,
     with _Stage(stage_events, "quantize_hact", st):
         if bufs.token_scale:
             nvfp4_quantize(bufs.hact, scale_mode=NV4_SCALE_ROW, out=bufs.hq, amax_out=bufs.hamax_rows, stream=stream)
+        elif bufs.hc is not None:
+            rt = bufs.routing
+            nvfp4_quantize(bufs.hact, layout=NV4_ROWS_AND_COLS, nseg=w.E, seg_offsets=rt.offsets,
+                           seg_padded_offsets=rt.padded_offsets, amax_in=bufs.hamax, out=bufs.hc, out_rows=bufs.hq,
+                           stream=stream)
         else:
             nvfp4_quantize(bufs.hact, amax_in=bufs.hamax, out=bufs.hq, stream=stream)
     with _Stage(stage_events, "gemm2", st):
@@ -596,10 +608,13 @@ def moe_backward(x: torch.Tensor, fwd: ForwardBuffers, wt: TransposedWeights, dY
     if not dual:
         with _Stage(stage_events, "quantize_cols_dy2", st):
             nvfp4_quantize(dY2, amax_in=bufs.dy2_amax, out=bufs.dy2c, sr_seed=sr2, **seg)
-    with _Stage(stage_events, "quantize_cols_hact", st):
-        nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=bufs.hc, **seg)
+    hc = fwd.hc
+    if hc is None:  # the forward did not produce the SwiGLU output's column form
+        hc = bufs.hc
+        with _Stage(stage_events, "quantize_cols_hact", st):
+            nvfp4_quantize(fwd.hact, amax_in=fwd.hamax, out=hc, **seg)
     with _Stage(stage_events, "wgrad_w2", st):
-        nvfp4_grouped_gemm(bufs.dy2c, bufs.hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
+        nvfp4_grouped_gemm(bufs.dy2c, hc, rt.padded_offsets, E, H, group_mode=NV4_GROUP_K, C=bufs.dw2,
                            ws=bufs.gemm_ws, stream=stream)
     if not dual:
         with _Stage(stage_events, "quantize_cols_dy13", st):

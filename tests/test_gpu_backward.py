@@ -86,6 +86,48 @@ def test_tiny_backward_stagewise(gpu_lib, dual):
     assert rel_frob(host(b.dw13), dw13_ref) <= TOL
 
 
+@pytest.mark.parametrize("cfg_name", ["tiny", "qwen3_bwd"])
+def test_forward_makes_the_swiglu_columns(gpu_lib, cfg_name):
+    """A forward that also produces the SwiGLU output's column form (one read of
+    Hact for its row and its column quantisation): the rows are the separate pass's
+    bytes, the columns are the oracle's segment-column quantisation of the GPU's own
+    Hact with the tensor scale of its amax (all of them at tiny size, sampled output
+    rows at 16384 tokens), and the backward that takes them gives the same weight
+    gradient as one that quantises Hact itself."""
+    cfg = synth.CONFIGS[cfg_name]
+    d = synth.layer_inputs(cfg, with_grads=True)
+    W13, W2 = dev_bf16(d["W13"]), dev_bf16(d["W2"])
+    w = gpu_lib.quantize_expert_weights(W13, W2)
+    wt = gpu_lib.quantize_expert_weights_t(W13, W2)
+    x, lg = dev_bf16(d["X"]), dev_f32(d["logits"])
+    f1 = gpu_lib.moe_forward(x, lg, w, cfg.k)
+    fb = gpu_lib.alloc_forward(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, hact_cols=True)
+    f2 = gpu_lib.moe_forward(x, lg, w, cfg.k, fb)
+    torch.cuda.synchronize()
+    for a, b in ((f1.hq.codes, f2.hq.codes), (f1.hq.scales, f2.hq.scales), (f1.hq.tscale, f2.hq.tscale),
+                 (f1.out, f2.out)):
+        assert torch.equal(a, b)
+    off = host(f2.routing.offsets).astype(np.int64)
+    po = host(f2.routing.padded_offsets).astype(np.int64)
+    A = float(host(f2.hamax)[0])
+    if cfg_name == "tiny":
+        ref, _ = Q.quantize_cols(host(f2.hact), off, amax=A)
+        _exact_cols(f2.hc, ref)
+    else:
+        r = synth.rng(11)
+        cols = np.sort(r.choice(cfg.I, 24, replace=False))
+        hcols = host(f2.hact[:, torch.as_tensor(cols, device=f2.hact.device)])
+        ref, _ = Q.quantize_cols(hcols, off, amax=A)
+        c, sc = _codes(f2.hc, cols, 0, int(po[-1]))
+        assert np.array_equal(c, ref.packed()) and np.array_equal(sc, ref.scales)
+        assert host(f2.hc.tscale)[0] == ref.G[0]
+    dY2, dY13 = dev_bf16(d["dY2"]), dev_bf16(d["dY13"])
+    b1 = gpu_lib.moe_backward(x, f1, wt, dY2, dY13)
+    b2 = gpu_lib.moe_backward(x, f2, wt, dY2, dY13)
+    torch.cuda.synchronize()
+    assert torch.equal(b1.dw2, b2.dw2) and torch.equal(b1.dw13, b2.dw13)
+
+
 def test_backward_bf16_dgrad_is_rne_of_f32(gpu_lib):
     cfg = synth.CONFIGS["tiny"]
     _, _, _, _, b32 = _layer(gpu_lib, cfg, torch.float32)
