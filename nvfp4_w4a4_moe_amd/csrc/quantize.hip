@@ -503,14 +503,18 @@ __global__ __launch_bounds__(kThreads) void k_amax_vec(const float *x, int64_t n
 //   NV4_COLS_BATCHED  matrix s (rows [s*m, (s+1)*m)) -> output rows s*C + c,
 //                     positions [0, m).
 // One workgroup transposes a tile of P positions x C columns through LDS:
-//   1. 16-byte coalesced loads of the tile's source rows (all loads of a lane in
-//      flight together), zero for padding, into LDS [position][column];
-//   2. one lane per column: read 16 values down the column, block amax, E4M3
-//      scale, 16 E2M1 codes, into an LDS out-tile;
-//   3. coalesced stores: 8 lanes write one output row's P/2 code bytes.
-// With ROWS_TOO (NV4_ROWS_AND_COLS) the same tile also yields the row-direction
-// quantisation of its rows (blocks of 16 columns), so the source is read once for
-// both operands of a tensor that feeds a data gradient and a weight gradient.
+//   1. coalesced loads of the tile's source rows, 8 elements per lane and pass (all
+//      passes in flight together), zero for padding;
+//   2. with ROWS_TOO (NV4_ROWS_AND_COLS) the row-direction quantisation of the
+//      tile's rows straight from those registers (the two lanes of a 16-element
+//      block exchange their half maxima), so the source is read once for both
+//      operands of a tensor that feeds a data gradient and a weight gradient;
+//   3. the tile into LDS [position][column], 16-byte units of a row XOR-permuted by
+//      the row so that reads along rows and down columns spread over the banks;
+//   4. column blocks: each thread reads 16 rows x (2 or 4) columns (one 4- or
+//      8-byte LDS read per row), block amax, E4M3 scale, 16 E2M1 codes per column,
+//      into an LDS out-tile;
+//   5. coalesced stores: 8 lanes write one output row's P/2 code bytes.
 constexpr int kSegLds = 256;       // segment offsets staged in LDS up to this many segments
 constexpr int kOutPitch = 72;       // LDS out-tile row pitch for 64 code bytes (+8 breaks bank aliasing)
 constexpr int kScalePitch = 12;
@@ -520,28 +524,35 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   typedef typename std::conditional<F32, float, uint16_t>::type T;
   static_assert(P == 128, "tiles of 128 positions (8 blocks)");
   constexpr int NB = P / 16;                          // blocks per column per tile
-  constexpr int kVec = 16 / sizeof(T);                // elements per 16-byte load
-  constexpr int kLanesPerRow = C / kVec;
+  constexpr int kRowBytes = C * (int)sizeof(T);       // bytes of a tile row
+  constexpr int kUnits = kRowBytes / 16;              // 16-byte units per tile row (a power of two)
+  static_assert((kUnits & (kUnits - 1)) == 0, "row units must be a power of two");
+  constexpr int kLanesPerRow = C / 8;                 // 8-element chunks per tile row
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
   constexpr int kPasses = P / kRowsPerPass;
-  constexpr int kColGroups = kThreads / C;            // threads per column in phase 2
-  constexpr int kBlkPerThread = NB / kColGroups;
+  constexpr int kPatchCols = C * NB / kThreads;       // columns per thread in the column phase
+  constexpr int kPatchGroups = C / kPatchCols;        // column groups per block row
+  constexpr int kReadBytes = kPatchCols * (int)sizeof(T);
+  static_assert(kReadBytes == 4 || kReadBytes == 8, "column reads of 4 or 8 bytes");
+  static_assert(kPatchGroups * NB == kThreads, "one column patch per thread");
   // The column output tile reuses the input tile's LDS once every read of the input
-  // is done (the column results wait in registers), so that four workgroups fit on
+  // is done (the column results wait in registers), so that more workgroups fit on
   // a CU and keep more loads in flight.
   struct OutTile {
     uint8_t codes[C][kOutPitch];
     uint8_t scales[C][kScalePitch];
   };
-  static_assert(sizeof(OutTile) <= sizeof(T) * P * C, "output tile fits in the input tile");
-  __shared__ __attribute__((aligned(16))) T tile[P][C];
-  OutTile &otile = *reinterpret_cast<OutTile *>(&tile[0][0]);
+  static_assert(sizeof(OutTile) <= (size_t)P * kRowBytes, "output tile fits in the input tile");
+  __shared__ __attribute__((aligned(16))) uint8_t tile[P * kRowBytes];
+  OutTile &otile = *reinterpret_cast<OutTile *>(&tile[0]);
   auto &ocodes = otile.codes;
   auto &oscales = otile.scales;
   __shared__ int64_t bsrc[NB];
   __shared__ int bnum[NB], bgrp[NB];
   __shared__ float inv_tab[128];
   __shared__ int seg_pad[kSegLds + 1], seg_off[kSegLds + 1];
+  // byte offset of 16-byte unit u of tile row `row`
+  auto unit_off = [](int row, int u) -> int { return row * kRowBytes + ((u ^ (row & (kUnits - 1))) << 4); };
 
   if (blockIdx.x == 0 && blockIdx.y == 0) write_group_scales(a);
   const float *A = amax_src(a);
@@ -612,129 +623,130 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     inv_tab[threadIdx.x] = threadIdx.x ? __fdiv_rn(S_tile, e4m3_to_f32(threadIdx.x)) : 0.0f;
   __syncthreads();
 
-  // 1. load the tile
-  {
-    const int lr = threadIdx.x / kLanesPerRow, lc = (threadIdx.x % kLanesPerRow) * kVec;
-    const bool col_ok = c0 + lc < Ccols;
-    uint4 v[kPasses];
+  bool bad = false;
+  // 1. load the tile: lane (lr, lch) takes 8 elements at column c0 + 8 lch of tile rows
+  // lr + i * kRowsPerPass
+  const int lr = threadIdx.x / kLanesPerRow, lch = threadIdx.x % kLanesPerRow;
+  const bool col_ok = c0 + lch * 8 < Ccols;
+  Chunk<F32> v[kPasses];
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const int pp = i * kRowsPerPass + lr;
+    const int j = pp >> 4, r = pp & 15;
+    v[i] = Chunk<F32>{};
+    if (col_ok && r < bnum[j]) v[i] = load_chunk<F32>(a.x, row_off(a, bsrc[j] + r) + c0 + lch * 8);
+  }
+  // 2. row blocks of the tile's valid rows (tensor scale) from the loaded registers:
+  // lanes 2m and 2m + 1 of a row hold the two halves of one 16-element block
+  if (ROWS_TOO) {
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
       const int pp = i * kRowsPerPass + lr;
       const int j = pp >> 4, r = pp & 15;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (col_ok && r < bnum[j]) {
-        const int64_t src = bsrc[j] + r;
-        const T *px = static_cast<const T *>(a.x) + row_off(a, src) + c0 + lc;
-        v[i] = *reinterpret_cast<const uint4 *>(px);
+      const bool ok = col_ok && r < bnum[j];
+      const int64_t orow = bsrc[j] + r;  // logical row of x
+      float vv[8];
+      unpack_chunk<F32>(v[i], vv);
+      Rand4 rnd;
+      if (SR) rnd = philox4x64_10((uint64_t)((c0 + lch * 8) >> 3), (uint64_t)orow, 0, 0, a.sr_seed);
+      uint32_t sf;
+      bool bad_row = false;
+      const uint32_t p = quant_half_block<SR>(vv, S_tile, inv_tab, sf, bad_row, &rnd);
+      if (ok) {
+        bad |= bad_row;
+        reinterpret_cast<uint32_t *>(a.codes2 + orow * (Ccols >> 1))[(c0 >> 3) + lch] = p;
+        if ((lch & 1) == 0) a.scales2[orow * (Ccols >> 4) + ((c0 + lch * 8) >> 4)] = (uint8_t)sf;
       }
     }
+  }
+  // 3. the tile into LDS
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i)
-      *reinterpret_cast<uint4 *>(&tile[i * kRowsPerPass + lr][lc]) = v[i];
+  for (int i = 0; i < kPasses; ++i) {
+    const int pp = i * kRowsPerPass + lr;
+#pragma unroll
+    for (int w = 0; w < (F32 ? 2 : 1); ++w)
+      *reinterpret_cast<uint4 *>(&tile[unit_off(pp, lch * (F32 ? 2 : 1) + w)]) = v[i].w[w];
   }
   __syncthreads();
 
-  bool bad = false;
   // rnd0 / rnd1: the Philox blocks of the 16 elements' positions (SR only)
-  auto quant16 = [&](const float v[16], float S, bool use_tab, uint32_t &lo, uint32_t &hi, const Rand4 &rnd0,
+  auto quant16 = [&](const float vv[16], float S, bool use_tab, uint32_t &lo, uint32_t &hi, const Rand4 &rnd0,
                      const Rand4 &rnd1) -> uint32_t {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float av = fabsf(v[i]);
+      const float av = fabsf(vv[i]);
       bad |= !(av <= 3.402823466e38f);
       m = fmaxf(m, av);
     }
     const uint32_t sf = e4m3_from_f32(__fmul_rn(div6_rn(m), S));
     const float inv = use_tab ? inv_tab[sf] : (sf ? __fdiv_rn(S, e4m3_to_f32(sf)) : 0.0f);
     if (SR) {
-      lo = pack_e2m1_sr8(v, inv, rnd0);
-      hi = pack_e2m1_sr8(v + 8, inv, rnd1);
+      lo = pack_e2m1_sr8(vv, inv, rnd0);
+      hi = pack_e2m1_sr8(vv + 8, inv, rnd1);
       return sf;
     }
     lo = 0;
     hi = 0;
-    lo = pack_e2m1_pair<0>(lo, __fmul_rn(v[0], inv), __fmul_rn(v[1], inv));
-    lo = pack_e2m1_pair<1>(lo, __fmul_rn(v[2], inv), __fmul_rn(v[3], inv));
-    lo = pack_e2m1_pair<2>(lo, __fmul_rn(v[4], inv), __fmul_rn(v[5], inv));
-    lo = pack_e2m1_pair<3>(lo, __fmul_rn(v[6], inv), __fmul_rn(v[7], inv));
-    hi = pack_e2m1_pair<0>(hi, __fmul_rn(v[8], inv), __fmul_rn(v[9], inv));
-    hi = pack_e2m1_pair<1>(hi, __fmul_rn(v[10], inv), __fmul_rn(v[11], inv));
-    hi = pack_e2m1_pair<2>(hi, __fmul_rn(v[12], inv), __fmul_rn(v[13], inv));
-    hi = pack_e2m1_pair<3>(hi, __fmul_rn(v[14], inv), __fmul_rn(v[15], inv));
+    lo = pack_e2m1_pair<0>(lo, __fmul_rn(vv[0], inv), __fmul_rn(vv[1], inv));
+    lo = pack_e2m1_pair<1>(lo, __fmul_rn(vv[2], inv), __fmul_rn(vv[3], inv));
+    lo = pack_e2m1_pair<2>(lo, __fmul_rn(vv[4], inv), __fmul_rn(vv[5], inv));
+    lo = pack_e2m1_pair<3>(lo, __fmul_rn(vv[6], inv), __fmul_rn(vv[7], inv));
+    hi = pack_e2m1_pair<0>(hi, __fmul_rn(vv[8], inv), __fmul_rn(vv[9], inv));
+    hi = pack_e2m1_pair<1>(hi, __fmul_rn(vv[10], inv), __fmul_rn(vv[11], inv));
+    hi = pack_e2m1_pair<2>(hi, __fmul_rn(vv[12], inv), __fmul_rn(vv[13], inv));
+    hi = pack_e2m1_pair<3>(hi, __fmul_rn(vv[14], inv), __fmul_rn(vv[15], inv));
     return sf;
   };
-  auto tval = [&](int pp, int cc) -> float {
-    const T t = tile[pp][cc];
-    return F32 ? (float)t : __uint_as_float((uint32_t)t << 16);
-  };
 
-  // 2. row blocks of the tile's valid rows (tensor scale): each thread one row and
-  // a run of 4 blocks of 16 columns (32 code bytes, 4 scale bytes)
-  if (ROWS_TOO) {
-    constexpr int kRunsPerRow = C / 64;
-    const int pp = threadIdx.x / kRunsPerRow, run = threadIdx.x % kRunsPerRow;
-    const int j = pp >> 4, r = pp & 15;
-    if (pp < P && r < bnum[j] && c0 + run * 64 < Ccols) {
-      const int64_t orow = bsrc[j] + r;  // logical row of x
-      uint32_t cw[8], sfw = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = tval(pp, run * 64 + b * 16 + i);
-        Rand4 r0, r1;
-        if (SR) {  // row orow of the row-direction output, columns c0 + run*64 + b*16 + [0, 16), stream 0
-          const uint64_t pc = (uint64_t)((c0 + run * 64 + b * 16) >> 3);
-          r0 = philox4x64_10(pc, (uint64_t)orow, 0, 0, a.sr_seed);
-          r1 = philox4x64_10(pc + 1, (uint64_t)orow, 0, 0, a.sr_seed);
-        }
-        const uint32_t sf = quant16(v, S_tile, true, cw[2 * b], cw[2 * b + 1], r0, r1);
-        sfw |= sf << (8 * b);
-      }
-      uint8_t *dst = a.codes2 + orow * (Ccols >> 1) + ((c0 + run * 64) >> 1);
-      *reinterpret_cast<uint4 *>(dst) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-      *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-      *reinterpret_cast<uint32_t *>(a.scales2 + orow * (Ccols >> 4) + ((c0 + run * 64) >> 4)) = sfw;
-    }
-  }
-  // 3. column blocks: lane = column, kColGroups threads per column share its blocks
-  // (results wait in registers until the input tile has been read in full)
-  uint32_t col_lo[kBlkPerThread], col_hi[kBlkPerThread], col_sf[kBlkPerThread];
+  // 4. column blocks: thread (block row jb, column group cg) takes columns
+  // cg * kPatchCols + [0, kPatchCols) of positions 16 jb + [0, 16)
+  const int jb = threadIdx.x / kPatchGroups, cg = threadIdx.x % kPatchGroups;
+  uint32_t col_lo[kPatchCols], col_hi[kPatchCols], col_sf[kPatchCols];
   {
-    const int c = threadIdx.x % C, grp = threadIdx.x / C;
+    typedef typename std::conditional<kReadBytes == 8, uint2, uint32_t>::type RT;
+    const int cb = cg * kReadBytes;  // byte column of the patch inside a tile row
+    RT raw[16];
 #pragma unroll
-    for (int jj = 0; jj < kBlkPerThread; ++jj) {
-      const int j = grp * kBlkPerThread + jj;
-      float v[16];
+    for (int i = 0; i < 16; ++i) {
+      const int row = 16 * jb + i;
+      raw[i] = *reinterpret_cast<const RT *>(&tile[unit_off(row, cb >> 4) + (cb & 15)]);
+    }
+    const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[jb]]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = tval(16 * j + i, c);
-      const float S = uniform ? S_tile : tensor_encode_scale(A[bgrp[j]]);
+    for (int q = 0; q < kPatchCols; ++q) {
+      float vv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i]);
+        vv[i] = F32 ? __uint_as_float(w[q])
+                    : __uint_as_float((q & 1) ? (w[q >> 1] & 0xFFFF0000u) : (w[q >> 1] << 16));
+      }
       uint32_t lo, hi;
       Rand4 r0, r1;
-      if (SR) {  // output row orow0 + c, positions p0 + 16 j + [0, 16), stream 1
-        const uint64_t pc = (uint64_t)((p0 >> 3) + 2 * j);
+      if (SR) {  // output row orow0 + c, positions p0 + 16 jb + [0, 16), stream 1
+        const int c = cg * kPatchCols + q;
+        const uint64_t pc = (uint64_t)((p0 >> 3) + 2 * jb);
         r0 = philox4x64_10(pc, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
         r1 = philox4x64_10(pc + 1, (uint64_t)(orow0 + c), 1, 0, a.sr_seed);
       }
-      col_sf[jj] = quant16(v, S, uniform, lo, hi, r0, r1);
-      col_lo[jj] = lo;
-      col_hi[jj] = hi;
+      col_sf[q] = quant16(vv, S, uniform, lo, hi, r0, r1);
+      col_lo[q] = lo;
+      col_hi[q] = hi;
     }
   }
   __syncthreads();
   {  // every read of the input tile is done: its LDS becomes the output tile
-    const int c = threadIdx.x % C, grp = threadIdx.x / C;
 #pragma unroll
-    for (int jj = 0; jj < kBlkPerThread; ++jj) {
-      const int j = grp * kBlkPerThread + jj;
-      *reinterpret_cast<uint2 *>(&ocodes[c][8 * j]) = make_uint2(col_lo[jj], col_hi[jj]);
-      oscales[c][j] = (uint8_t)col_sf[jj];
+    for (int q = 0; q < kPatchCols; ++q) {
+      const int c = cg * kPatchCols + q;
+      *reinterpret_cast<uint2 *>(&ocodes[c][8 * jb]) = make_uint2(col_lo[q], col_hi[q]);
+      oscales[c][jb] = (uint8_t)col_sf[q];
     }
     __syncthreads();
   }
 
-  // 4. coalesced stores: 8 lanes per output row, one block (8 code bytes) each
+  // 5. coalesced stores: 8 lanes per output row, one block (8 code bytes) each
   {
     const int j = threadIdx.x & 7, rr = threadIdx.x >> 3;
     const bool blk_ok = p0 + 16 * j < plimit;
