@@ -319,12 +319,14 @@ def time_recipe(nv4, torch, np, cfg, inp, recipe, part, args, stages: bool, flus
     nvfp4_fwd = recipe != "bf16"
     backward = part != "fwd"
 
+    f16 = args.weights_f16  # keep the decoded FP16 weights next to the NVFP4 ones
+
     def prep():
-        w = nv4.quantize_expert_weights(W13, W2) if nvfp4_fwd else None
+        w = nv4.quantize_expert_weights(W13, W2, f16=f16 and recipe != "dequantized") if nvfp4_fwd else None
         wt = None
         if backward:
             if recipe in ("nvfp4", "nvfp4-sr"):
-                wt = nv4.quantize_expert_weights_t(W13, W2)
+                wt = nv4.quantize_expert_weights_t(W13, W2, f16=f16)
             elif recipe == "dequantized":
                 wt = nv4.dequantize_expert_weights_t(w)
             else:
@@ -557,6 +559,10 @@ def main():
                     help="the workload of the JSON line: the learner batch forward + backward (default), the "
                          "16384-token forward, the same layer's backward, or the dense 8192x2048x768 GEMM")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--weights-f16", action="store_true",
+                    help="keep each NVFP4 weight tensor's exact decoded FP16 values (made with the weight "
+                         "quantisation, once per optimizer step), which the grouped GEMMs read instead of "
+                         "decoding the weights")
     ap.add_argument("--token-scale", action="store_true",
                     help="per-token FP32 scales for X and the SwiGLU output instead of one per tensor")
     ap.add_argument("--no-cpu-baseline", action="store_true")

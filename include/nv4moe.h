@@ -127,6 +127,12 @@ typedef struct nv4_tensor {
   int64_t K;
   int32_t scale_mode;
   int32_t nseg;
+  /* Optional (NULL when absent): the tensor's exact FP16 values without the decode
+   * scale, e2m1(code) * e4m3(block scale) for every element, [rows][K] row-major,
+   * 16-byte aligned (nvfp4_decode_f16 makes them).  Only B of a GROUP_M
+   * nvfp4_grouped_gemm reads them (see there); codes, scales and tscale stay
+   * required. */
+  const uint16_t *f16;
 } nv4_tensor;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -341,6 +347,12 @@ nv4_status moe_permute_noalloc(const float *logits, int64_t T, int E, int k, int
  *              Calls that share a workspace must not overlap.
  * K (A->K == B->K) must be a positive multiple of 16 ([4BL] "Baseline": blocks of 16);
  * GROUP_K ranges must be 16-aligned.
+ * B->f16 (decoded weights): with GROUP_M, a per-tensor A scale and K % 64 == 0 the
+ * kernel reads B's elements from B->f16 instead of decoding codes and scales (the
+ * same exact FP16 values; B->tscale still applies, per tensor, expert, projection or
+ * K half as above).  The products are the same; only the grouping of K inside the
+ * FP32 accumulation differs (stages of 64 instead of 128), so the two results agree
+ * to FP32 rounding.  Otherwise B->f16 is ignored.
  * Errors: EINVAL, EALIGN (K not a positive multiple of 16, A->K != B->K, misaligned
  * codes), EUNSUPPORTED (SWIGLU with GROUP_K, row scales with GROUP_K, a B scale
  * grouping other than those above), EWORKSPACE (K % 64 != 0 without the workspace),
@@ -352,6 +364,21 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
                               int group_mode, int epilogue,
                               void *C, nv4_dtype ctype, int64_t ldc, float *amax_out,
                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * nvfp4_decode_f16 -- the exact FP16 values of an NVFP4 tensor without its decode
+ * scale: out[r][k] = e2m1(code) * e4m3(block scale), which has at most 6
+ * significant bits and lies in [2^-10, 2688], so FP16 holds it exactly.  [4BL]
+ * "Improving Gradient Stability": a GEMM consumes the dequantised operand; the
+ * expert weights change once per optimizer step, so their decoded values can be
+ * kept (nv4_tensor.f16) instead of decoded inside every grouped GEMM.
+ *   q      NVFP4 tensor [q->rows][q->K], K % 16 == 0 (any scale grouping: tscale is
+ *          not read).
+ *   out    device FP16 [q->rows][ldo], ldo >= K, ldo % 8 == 0, 16-byte aligned.
+ * Errors: EINVAL (NULL pointers, bad sizes), EALIGN (K % 16, ldo % 8, misaligned
+ * pointers), EHIP.
+ */
+nv4_status nvfp4_decode_f16(const nv4_tensor *q, void *out, int64_t ldo, void *stream);
 
 /*
  * nv4_to_bf16 -- BF16 operands for the BF16 and dequantized backward.

@@ -53,7 +53,7 @@ class NV4Error(RuntimeError):
 class NV4Tensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tscale", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("K", ctypes.c_int64), ("scale_mode", ctypes.c_int32),
-                ("nseg", ctypes.c_int32)]
+                ("nseg", ctypes.c_int32), ("f16", ctypes.c_void_p)]
 
 
 _lib = None
@@ -79,6 +79,7 @@ _SIGS = {
     "nvfp4_grouped_gemm": (_I, [ctypes.POINTER(NV4Tensor), ctypes.POINTER(NV4Tensor), _P, _I, _I64, _I64, _P,
                                 _I, _I, _P, _I, _I64, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _I, _I64, _P, _P, _I64, _I, _I64, _P, _I, _P]),
+    "nvfp4_decode_f16": (_I, [ctypes.POINTER(NV4Tensor), _P, _I64, _P]),
     "nv4_to_bf16": (_I, [_P, _I64, _I64, ctypes.POINTER(NV4Tensor), _I64, _I64, _P, _I, _I, _P, _P, _P, _I64, _I64,
                          _P]),
     "bf16_grouped_gemm": (_I, [_P, _I64, _P, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I, _P, _I, _I64, _P, _P, _SZ,
@@ -140,6 +141,7 @@ class NVFP4:
     K: int
     scale_mode: int = NV4_SCALE_TENSOR
     nseg: int = 1
+    f16: torch.Tensor | None = None  # exact FP16 values without the decode scale (nvfp4_decode_f16), or None
 
     @staticmethod
     def empty(rows: int, K: int, ngroups: int = 1, device="cuda") -> "NVFP4":
@@ -149,7 +151,8 @@ class NVFP4:
 
     def c(self) -> NV4Tensor:
         return NV4Tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(),
-                         self.rows, self.K, self.scale_mode, self.nseg)
+                         self.rows, self.K, self.scale_mode, self.nseg,
+                         None if self.f16 is None else self.f16.data_ptr())
 
 
 def _ngroups(rows, scale_mode, nseg):
@@ -205,10 +208,30 @@ def nvfp4_quantize(x: torch.Tensor, layout: int = NV4_ROWS, scale_mode: int = NV
     else:
         _check(lib.nvfp4_quantize_sr(*args, ctypes.c_uint64(sr_seed & (2 ** 64 - 1)), _stream(stream)))
     out.scale_mode, out.nseg = d.scale_mode, d.nseg
+    if out.f16 is not None:  # keep an attached FP16 copy in step with the new codes
+        nvfp4_decode_f16(out, out=out.f16, stream=stream)
     if d2 is not None:
         out_rows.scale_mode, out_rows.nseg = d2.scale_mode, d2.nseg
         out.rows_out = out_rows
     return out
+
+
+def nvfp4_decode_f16(q: NVFP4, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Exact FP16 values e2m1 * e4m3 of q's elements, [rows, K] (the decode scale G
+    not applied)."""
+    if out is None:
+        out = torch.empty((q.rows, q.K), dtype=torch.float16, device=q.codes.device)
+    assert out.dtype == torch.float16 and out.dim() == 2 and out.stride(1) == 1
+    d = q.c()
+    _check(load().nvfp4_decode_f16(ctypes.byref(d), _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def with_f16(q: NVFP4, stream=None) -> NVFP4:
+    """q with its decoded FP16 values attached (the grouped GEMM then reads a GROUP_M
+    B operand from them instead of decoding it)."""
+    q.f16 = nvfp4_decode_f16(q, stream=stream)
+    return q
 
 
 def nv4_amax(x: torch.Tensor, amax: torch.Tensor | None = None, dev_status: torch.Tensor | None = None,
@@ -363,12 +386,16 @@ class ExpertWeights:
     I: int
 
 
-def quantize_expert_weights(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> ExpertWeights:
+def quantize_expert_weights(W13: torch.Tensor, W2: torch.Tensor, f16: bool = False, stream=None) -> ExpertWeights:
     """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> NVFP4 with one scale per expert and
-    projection (gate, up and down)."""
+    projection (gate, up and down).  f16: also keep each tensor's exact decoded FP16
+    values, which the grouped GEMMs then read instead of decoding the weights."""
     E, I2, H = W13.shape
     w13 = nvfp4_quantize(W13.reshape(E * I2, H), scale_mode=NV4_SCALE_SEGMENT, nseg=2 * E, stream=stream)
     w2 = nvfp4_quantize(W2.reshape(E * H, I2 // 2), scale_mode=NV4_SCALE_SEGMENT, nseg=E, stream=stream)
+    if f16:
+        with_f16(w13, stream)
+        with_f16(w2, stream)
     return ExpertWeights(w13, w2, E, H, I2 // 2)
 
 
@@ -506,13 +533,18 @@ class TransposedWeights:
     w13t: NVFP4
 
 
-def quantize_expert_weights_t(W13: torch.Tensor, W2: torch.Tensor, stream=None) -> TransposedWeights:
-    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> per-expert transposes in NVFP4."""
+def quantize_expert_weights_t(W13: torch.Tensor, W2: torch.Tensor, f16: bool = False,
+                              stream=None) -> TransposedWeights:
+    """W13 [E, 2I, H] and W2 [E, H, I] (BF16) -> per-expert transposes in NVFP4 (f16:
+    with their exact decoded FP16 values, as quantize_expert_weights)."""
     E, I2, H = W13.shape
     w2t = nvfp4_quantize(W2.reshape(E * H, I2 // 2), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT,
                          nseg=E, stream=stream)
     w13t = nvfp4_quantize(W13.reshape(E * I2, H), layout=NV4_COLS_BATCHED, scale_mode=NV4_SCALE_SEGMENT_HALVES,
                           nseg=E, stream=stream)
+    if f16:
+        with_f16(w2t, stream)
+        with_f16(w13t, stream)
     return TransposedWeights(w2t, w13t)
 
 

@@ -24,7 +24,7 @@ ARCH = os.environ.get("NV4_OFFLOAD_ARCH", "gfx950")
 
 # the grouped GEMM's instantiations come first: they take the longest to compile
 SOURCES = ["gemm_m_swiglu.hip", "gemm_m.hip", "gemm_k.hip", "gemm_m_ksplit.hip", "gemm_m_swiglu_rows.hip", "gemm_m_rows.hip",
-           "gemm_m_small.hip",
+           "gemm_m_small.hip", "gemm_m_wf16.hip", "gemm_m_wf16_ksplit.hip",
            "gemm_bf16.hip", "gemm.hip", "quantize.hip", "permute.hip", "convert.hip", "combine.hip", "ceilings.hip", "api.cpp"]
 
 HIP_FLAGS = [

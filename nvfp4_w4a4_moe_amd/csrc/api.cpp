@@ -448,6 +448,13 @@ nv4_status nvfp4_grouped_gemm(const nv4_tensor *A, const nv4_tensor *B, const in
       return fail(NV4_EINVAL, "nvfp4_grouped_gemm: C must stay below 2^31 elements");
     g.N = B->rows;
   }
+  // exact FP16 B (decoded weights): GROUP_M, one tensor scale for A, whole 64-wide stages
+  if (B->f16 && group_mode == NV4_GROUP_M && A->scale_mode == NV4_SCALE_TENSOR && A->K % 64 == 0) {
+    if (!aligned(B->f16, 16)) return fail(NV4_EALIGN, "nvfp4_grouped_gemm: B->f16 must be 16-byte aligned");
+    if (B->rows * A->K * 2 >= (1ll << 32))
+      return fail(NV4_EINVAL, "nvfp4_grouped_gemm: B->f16 must stay below 4 GiB");
+    g.b_f16 = B->f16;
+  }
   if (repack) {
     // zero-padded copies of both operands, then the GEMM on K = Kp (padded blocks carry
     // scale 0 and add exact zeros)
@@ -535,6 +542,20 @@ nv4_status bf16_grouped_gemm(const void *A, int64_t a_rows_n, const void *B, int
 }
 
 // ---------------------------------------------------------------- BF16 operands
+
+nv4_status nvfp4_decode_f16(const nv4_tensor *q, void *out, int64_t ldo, void *stream) {
+  if (!q) return fail(NV4_EINVAL, "nvfp4_decode_f16: q is NULL");
+  if (q->rows < 0 || q->K < 0) return fail(NV4_EINVAL, "nvfp4_decode_f16: negative shape");
+  if (q->K % 16) return fail(NV4_EALIGN, "nvfp4_decode_f16: K = %lld is not a multiple of 16", (long long)q->K);
+  if (ldo < q->K || ldo % 8) return fail(NV4_EALIGN, "nvfp4_decode_f16: ldo must be >= K and a multiple of 8");
+  if (q->rows == 0 || q->K == 0) return NV4_OK;
+  if (!q->codes || !q->scales || !out) return fail(NV4_EINVAL, "nvfp4_decode_f16: NULL buffer");
+  if (!aligned(q->codes, 8) || !aligned(out, 16))
+    return fail(NV4_EALIGN, "nvfp4_decode_f16: codes must be 8-byte and out 16-byte aligned");
+  return from_hip(nv4::launch_decode_f16(q->codes, q->scales, q->rows, q->K, static_cast<uint16_t *>(out), ldo,
+                                         static_cast<hipStream_t>(stream)),
+                  "nvfp4_decode_f16");
+}
 
 nv4_status nv4_to_bf16(const void *x, int64_t x_rows, int64_t ldx, const nv4_tensor *q, int64_t rows, int64_t K,
                        const int32_t *row_index, int layout, int nseg, const int32_t *seg_offsets,

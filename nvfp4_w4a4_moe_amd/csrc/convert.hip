@@ -150,7 +150,32 @@ __global__ __launch_bounds__(256) void k_cols_bf16(ConvertArgs a) {
   }
 }
 
+// Exact FP16 values e2m1 * e4m3 of an NVFP4 tensor (the decode scale G not applied):
+// one thread per 16-element block, 8 code bytes and 1 scale byte in, 32 bytes out.
+__global__ __launch_bounds__(256) void k_decode_f16(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                                    int64_t K, uint16_t *out, int64_t ldo) {
+  const int64_t nb = K >> 4, total = rows * nb;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / nb, b = i - r * nb;
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + r * (K >> 1) + b * 8);
+    const f16x2 s2 = e4m3x2_to_f16<false>((uint32_t)scales[r * nb + b] * 0x0101u);
+    const f16x8 lo = decode8_f16(c.x, s2), hi = decode8_f16(c.y, s2);
+    uint4 *o = reinterpret_cast<uint4 *>(out + r * ldo + b * 16);
+    o[0] = __builtin_bit_cast(uint4, lo);
+    o[1] = __builtin_bit_cast(uint4, hi);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_f16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K, uint16_t *out,
+                             int64_t ldo, hipStream_t stream) {
+  const int64_t total = rows * (K >> 4);
+  if (total == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, (int64_t)device_cu_count() * 16);
+  k_decode_f16<<<grid, 256, 0, stream>>>(codes, scales, rows, K, out, ldo);
+  return hipGetLastError();
+}
 
 hipError_t launch_convert(const ConvertArgs &a, hipStream_t stream) {
   const bool fp4 = a.codes != nullptr;

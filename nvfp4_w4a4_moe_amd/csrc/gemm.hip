@@ -2,7 +2,7 @@
 // the operand type, group mode, epilogue and A-scale mode.  The kernel is in
 // gemm_kernel.h; its instantiations are compiled in gemm_m.hip, gemm_m_rows.hip,
 // gemm_m_swiglu.hip, gemm_m_swiglu_rows.hip, gemm_m_ksplit.hip, gemm_m_small.hip,
-// gemm_k.hip and gemm_bf16.hip.
+// gemm_m_wf16.hip, gemm_m_wf16_ksplit.hip, gemm_k.hip and gemm_bf16.hip.
 #include <algorithm>
 
 #include "nv4_internal.h"
@@ -18,6 +18,8 @@ hipError_t launch_gemm_k(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_m_ksplit(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_m_small(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_m_wf16(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_gemm_m_wf16_ksplit(const GemmArgs &g, hipStream_t stream);
 
 namespace {
 
@@ -56,6 +58,9 @@ hipError_t launch_repack_k(const uint8_t *codes, const uint8_t *scales, int64_t 
 
 hipError_t launch_grouped_gemm(const GemmArgs &g, hipStream_t stream) {
   if (g.operands_bf16) return launch_gemm_bf16(g, stream);
+  if (g.b_f16)  // exact FP16 B (GROUP_M, one tensor scale for A, K % 64 == 0: checked by the caller)
+    return g.b_scale_mode == NV4_SCALE_SEGMENT_HALVES ? launch_gemm_m_wf16_ksplit(g, stream)
+                                                      : launch_gemm_m_wf16(g, stream);
   const bool rows = g.a_scale_mode == NV4_SCALE_ROW;
   if (g.group_mode == NV4_GROUP_K) return launch_gemm_k(g, stream);
   if (g.b_scale_mode == NV4_SCALE_SEGMENT_HALVES) return launch_gemm_m_ksplit(g, stream);

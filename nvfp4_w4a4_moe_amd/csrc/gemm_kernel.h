@@ -28,6 +28,12 @@
 // 4-byte read the scale bytes of all four of its blocks in the stage.  Any
 // permutation of K applied to both operands leaves the dot product unchanged.
 //
+// Decoded weights (B given as its exact FP16 values e2m1 * e4m3, GROUP_M only): A stays
+// NVFP4 and is decoded as above, B is read from LDS as it is.  Stages of 64 (an FP16 B
+// stage of 128 would not fit twice in LDS next to A), 64 x 128 wave tiles so that
+// each wave decodes two A fragments per eight MFMAs.  The products are the same; the
+// grouping of K in the FP32 sums differs.
+//
 // BF16 operands (the unquantised layer and the BF16 / dequantized backward of
 // "The 4-bitter Lesson", section "Improving Gradient Stability") use the same
 // kernel with the decode removed: stages of 32 BF16 elements (64 bytes per row,
@@ -56,19 +62,23 @@ constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int WAVES_M, int WAVES_N, int FM, int FN, int WAVES_PER_SIMD = 1, int STAGES = 2, bool BF16 = false>
+template <int WAVES_M, int WAVES_N, int FM, int FN, int WAVES_PER_SIMD = 1, int STAGES = 2, bool BF16 = false,
+          bool WF16 = false>
 struct TileCfg {
   static constexpr bool kBf16 = BF16;                   // operands BF16 (else NVFP4)
+  static constexpr bool kWf16 = WF16;                   // A NVFP4, B exact FP16 values (decoded weights)
   static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N, kFM = FM, kFN = FN;
   static constexpr int kWavesPerSimd = WAVES_PER_SIMD;  // occupancy the registers are budgeted for
   static constexpr int kStages = STAGES;                // LDS ring depth (prefetch distance STAGES - 1)
   static constexpr int BM = WAVES_M * FM * 32;
   static constexpr int BN = WAVES_N * FN * 32;  // rows of B per tile
-  static constexpr int BK = BF16 ? 32 : 128;    // K per LDS stage
+  static constexpr int BK = BF16 ? 32 : (WF16 ? 64 : 128);  // K per LDS stage
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
-  static constexpr int kRowBytes = BF16 ? BK * 2 : BK / 2;  // element bytes per row per stage (64)
-  static constexpr int kScBytes = BF16 ? 0 : BK / 16;       // scale bytes per row per stage
-  static constexpr int kStageBytes = (BM + BN) * (kRowBytes + kScBytes);
+  static constexpr int kRowBytes = BF16 ? BK * 2 : BK / 2;  // A element bytes per row per stage
+  static constexpr int kScBytes = BF16 ? 0 : BK / 16;       // A scale bytes per row per stage
+  static constexpr int kRowBytesB = (BF16 || WF16) ? BK * 2 : BK / 2;  // B element bytes per row per stage
+  static constexpr int kScBytesB = (BF16 || WF16) ? 0 : BK / 16;       // B scale bytes per row per stage
+  static constexpr int kStageBytes = BM * (kRowBytes + kScBytes) + BN * (kRowBytesB + kScBytesB);
 };
 
 // an index into A taken from the caller: clamp into [0, rows) so that an index
@@ -236,13 +246,20 @@ void k_gemm(GemmArgs g) {
   // LDS DMA plan: codes in 1 KB blocks of 16 rows, scales in 256-byte blocks of 32
   // rows (A rows first, then B rows); wave w issues blocks w, w + NW, ...
   constexpr bool BF = Cfg::kBf16;
-  constexpr int kCodeBlocks = (BM + BN) / 16, kScBlocks = BF ? 0 : (BM + BN) / 32;
+  // WF: A NVFP4 stages of 64 codes (32 bytes, 4 scale bytes per row), B exact FP16
+  // values (128 bytes per row); 1 KB DMA blocks of 32 A rows or 8 B rows, A scales in
+  // 256-byte blocks of 64 rows
+  constexpr bool WF = Cfg::kWf16;
+  static_assert(!WF || (GROUP == NV4_GROUP_M && FM == 2 && FN == 4), "FP16 B: GROUP_M, 64 x 128 wave tiles");
+  constexpr int kCodeBlocksA = WF ? BM * RB / 1024 : 0;
+  constexpr int kCodeBlocks = WF ? kCodeBlocksA + BN * Cfg::kRowBytesB / 1024 : (BM + BN) / 16;
+  constexpr int kScBlocks = BF ? 0 : (WF ? BM * SB / 256 : (BM + BN) / 32);
   constexpr int kCodeIters = (kCodeBlocks + NW - 1) / NW;
   constexpr int kScIters = BF ? 1 : (kScBlocks + NW - 1) / NW;
   // DMAs every wave issues per stage (the vmcnt wait uses the smallest count)
   constexpr int kDmaMin = kCodeBlocks / NW + kScBlocks / NW;
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows must be multiples of 32");
-  constexpr int kScBase = (BM + BN) * RB;
+  constexpr int kScBase = WF ? BM * RB + BN * Cfg::kRowBytesB : (BM + BN) * RB;
   constexpr int S = Cfg::kStages;
   static_assert(S >= 2 && S <= 4, "LDS ring of 2 to 4 stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[Cfg::kStageBytes];
@@ -262,9 +279,11 @@ void k_gemm(GemmArgs g) {
   const int E = g.E;
   const int64_t K = g.K;
   const int64_t ldA = BF ? K * 2 : K >> 1, ldAs = K >> 4;  // bytes per row: elements (codes), scales
+  const int64_t ldB = (BF || WF) ? K * 2 : K >> 1;          // bytes per B row
   // buffer resources: loads past num_records return zeros (operands are < 4 GiB)
   const uint32_t na_c = (uint32_t)(g.a_rows * ldA), na_s = (uint32_t)(g.a_rows * ldAs);
-  const uint32_t nb_c = (uint32_t)(g.b_rows * ldA), nb_s = (uint32_t)(g.b_rows * ldAs);
+  const uint32_t nb_c = (uint32_t)(g.b_rows * ldB), nb_s = (uint32_t)(g.b_rows * ldAs);
+  const void *b_elems = WF ? static_cast<const void *>(g.b_f16) : static_cast<const void *>(g.b_codes);
 
   // ---- tile space
   int64_t total;
@@ -376,23 +395,45 @@ void k_gemm(GemmArgs g) {
     uint32_t c_off[kCodeIters];
 #pragma unroll
     for (int j = 0; j < kCodeIters; ++j) {
-      const int row = (j * NW + wave) * 16 + (lane >> 2);
-      const bool isA = row < BM;  // uniform over the wave
-      const int r = isA ? row : row - BM;
-      const int q = swz(lane & 3, r);  // chunk that lands in this lane's slot (swz is its own inverse)
-      int64_t pr = -1;
-      if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
-      c_off[j] = pr >= 0 ? (uint32_t)(pr * ldA) + q * 16 : (isA ? na_c : nb_c);
+      if constexpr (WF) {
+        const int blk = j * NW + wave;
+        if (blk < kCodeBlocksA) {  // 32 A rows of 32 code bytes: lane -> row lane/2, chunk lane%2
+          const int r = blk * 32 + (lane >> 1);
+          const int64_t pr = a_row_of(g, job, r);
+          c_off[j] = pr >= 0 ? (uint32_t)(pr * ldA) + (lane & 1) * 16 : na_c;
+        } else {  // 8 B rows of 128 value bytes; the lane's slot holds chunk slot ^ (row % 8)
+          const int r = (blk - kCodeBlocksA) * 8 + (lane >> 3);
+          const int q = (lane & 7) ^ (r & 7);
+          int64_t pr = -1;
+          if (r < BN) pr = b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
+          c_off[j] = pr >= 0 ? (uint32_t)(pr * ldB) + q * 16 : nb_c;
+        }
+      } else {
+        const int row = (j * NW + wave) * 16 + (lane >> 2);
+        const bool isA = row < BM;  // uniform over the wave
+        const int r = isA ? row : row - BM;
+        const int q = swz(lane & 3, r);  // chunk that lands in this lane's slot (swz is its own inverse)
+        int64_t pr = -1;
+        if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
+        c_off[j] = pr >= 0 ? (uint32_t)(pr * ldA) + q * 16 : (isA ? na_c : nb_c);
+      }
     }
     uint32_t s_off[kScIters];
 #pragma unroll
     for (int j = 0; j < (BF ? 0 : kScIters); ++j) {
-      const int row = (j * NW + wave) * 32 + (lane >> 1);
-      const bool isA = row < BM;
-      const int r = isA ? row : row - BM;
-      int64_t pr = -1;
-      if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
-      s_off[j] = pr >= 0 ? (uint32_t)(pr * ldAs) + (lane & 1) * 4 : (isA ? na_s : nb_s);
+      if constexpr (WF) {  // 64 A rows of 4 scale bytes
+        const int r = (j * NW + wave) * 64 + lane;
+        int64_t pr = -1;
+        if (r < BM) pr = a_row_of(g, job, r);
+        s_off[j] = pr >= 0 ? (uint32_t)(pr * ldAs) : na_s;
+      } else {
+        const int row = (j * NW + wave) * 32 + (lane >> 1);
+        const bool isA = row < BM;
+        const int r = isA ? row : row - BM;
+        int64_t pr = -1;
+        if (row < BM + BN) pr = isA ? a_row_of(g, job, r) : b_row_of<GROUP, EPI, FN, BN>(g, job, nt_idx, r);
+        s_off[j] = pr >= 0 ? (uint32_t)(pr * ldAs) + (lane & 1) * 4 : (isA ? na_s : nb_s);
+      }
     }
 
     // ---- K range in stages of BK (stage starts 128-aligned; blocks outside
@@ -403,23 +444,24 @@ void k_gemm(GemmArgs g) {
     auto issue = [&](int kt, uint8_t *dst) {
       // element (code) byte offset of the stage
       const uint32_t kc = (uint32_t)(BF ? (kb0 + (int64_t)kt * BK) * 2 : (kb0 + (int64_t)kt * BK) >> 1);
+      const uint32_t kcb = WF ? (uint32_t)((kb0 + (int64_t)kt * BK) * 2) : kc;  // B element byte offset
       const uint32_t ks = (uint32_t)((kb0 + (int64_t)kt * BK) >> 4);  // scale byte offset of the stage
 #pragma unroll
       for (int j = 0; j < kCodeIters; ++j) {
         const int blk = j * NW + wave;
         if (kCodeBlocks % NW != 0 && blk >= kCodeBlocks) break;
-        const bool isA = blk * 16 < BM;
+        const bool isA = WF ? blk < kCodeBlocksA : blk * 16 < BM;
         // a chunk past the row end reads the next row (finite codes); the scale
         // mask in compute() zeroes those blocks.  Past the operand's end the buffer
         // returns zeros.
         if (isA) dma16_to_lds(g.a_codes, na_c, dst + blk * 1024, c_off[j] + kc);
-        else dma16_to_lds(g.b_codes, nb_c, dst + blk * 1024, c_off[j] + kc);
+        else dma16_to_lds(b_elems, nb_c, dst + blk * 1024, c_off[j] + kcb);
       }
 #pragma unroll
       for (int j = 0; j < (BF ? 0 : kScIters); ++j) {
         const int blk = j * NW + wave;
         if (kScBlocks % NW != 0 && blk >= kScBlocks) break;
-        const bool isA = blk * 32 < BM;
+        const bool isA = WF || blk * 32 < BM;
         if (isA) dma4_to_lds(g.a_scales, na_s, dst + kScBase + blk * 256, s_off[j] + ks);
         else dma4_to_lds(g.b_scales, nb_s, dst + kScBase + blk * 256, s_off[j] + ks);
       }
@@ -457,8 +499,13 @@ void k_gemm(GemmArgs g) {
     // h*64 + [0, 64): slice `sub` is chunk 2h + sub (32 codes, one 16-byte read) and
     // scale bytes 4h + 2 sub + {0, 1}; MFMA step t = sub*4 + s consumes dword s of
     // the slice with the scale of block s/2.
+    // FP16 B (WF): stages of 64; A as one slice (lane half h: elements h*32 + [0, 32), one
+    // 16-byte read, scale bytes 2h and 2h + 1); MFMA step s takes elements h*32 + s*8 +
+    // [0, 8) of both operands, for B one 16-byte read of chunk 4h + s of the fragment
+    // row (chunks XOR-permuted by the row's low three bits).
     constexpr int kSubs = BF ? 1 : BK / 64, kSteps = BK / 16;  // (NVFP4 only)
-    static_assert(BF || kSubs == 2, "NVFP4 stages of 128 codes");
+    static_assert(BF || (WF ? kSubs == 1 : kSubs == 2), "NVFP4 stages of 128 codes (64 with FP16 B)");
+    const uint8_t *lds_cur = lds0;  // the stage being computed (FP16 B is read step by step)
     uint4 ca[kSubs][FM], cb[kSubs][FN];
     f16x2 sa[kSubs][FM], sbv[kSubs][FN];
     // per-lane byte offsets inside a stage: the lane's fragment row (l32 of the
@@ -471,50 +518,83 @@ void k_gemm(GemmArgs g) {
     const int soffA = kScBase + rowA * SB + 4 * h, soffB = kScBase + rowB * SB + 4 * h;
     auto lds_read = [&](const uint8_t *base, int kt, auto full_c) {
       constexpr bool kFull = decltype(full_c)::value;
-      // scale-byte mask of this lane's four blocks (k0 + h*64 + b*16, b = 0..3) when
-      // the stage is partial: blocks outside [k_lo, k_hi) decode to zero
-      uint32_t smask = 0xFFFFFFFFu;
-      if (!kFull) {
-        const int64_t kb = kb0 + (int64_t)kt * BK + h * 64;
-        smask = 0;
+      if constexpr (WF) {  // full stages only (K % 64 == 0, GROUP_M)
+        const int rA = wm * FM * 32 + l32;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (kb + 16 * b >= job.k_lo && kb + 16 * b < job.k_hi) smask |= 0xFFu << (8 * b);
+        for (int i = 0; i < FM; ++i) {
+          ca[0][i] = *reinterpret_cast<const uint4 *>(base + (rA + i * 32) * RB + h * 16);
+          const uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + kScBase + (rA + i * 32) * SB);
+          sa[0][i] = e4m3x2_to_f16<false>(s4 >> (16 * h));
+        }
+      } else {
+        // scale-byte mask of this lane's four blocks (k0 + h*64 + b*16, b = 0..3) when
+        // the stage is partial: blocks outside [k_lo, k_hi) decode to zero
+        uint32_t smask = 0xFFFFFFFFu;
+        if (!kFull) {
+          const int64_t kb = kb0 + (int64_t)kt * BK + h * 64;
+          smask = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (kb + 16 * b >= job.k_lo && kb + 16 * b < job.k_hi) smask |= 0xFFu << (8 * b);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          ca[0][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch0);
+          ca[1][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch1);
+          uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffA + i * 32 * SB);
+          if (!kFull) s4 &= smask;
+          sa[0][i] = e4m3x2_to_f16<false>(s4);
+          sa[1][i] = e4m3x2_to_f16<true>(s4);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          cb[0][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch0);
+          cb[1][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch1);
+          uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffB + j * 32 * SB);
+          if (!kFull) s4 &= smask;
+          sbv[0][j] = e4m3x2_to_f16<false>(s4);
+          sbv[1][j] = e4m3x2_to_f16<true>(s4);
+        }
       }
+    };
+    // FP16 B: A fragments of MFMA step st decoded, B fragments read as they are
+    auto decode_a = [&](int st, f16x8 (&av)[FM]) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        ca[0][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch0);
-        ca[1][i] = *reinterpret_cast<const uint4 *>(base + offA + i * 32 * RB + ch1);
-        uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffA + i * 32 * SB);
-        if (!kFull) s4 &= smask;
-        sa[0][i] = e4m3x2_to_f16<false>(s4);
-        sa[1][i] = e4m3x2_to_f16<true>(s4);
+        const uint32_t w = st == 0 ? ca[0][i].x : st == 1 ? ca[0][i].y : st == 2 ? ca[0][i].z : ca[0][i].w;
+        const f16x2 sc = st < 2 ? __builtin_shufflevector(sa[0][i], sa[0][i], 0, 0)
+                                : __builtin_shufflevector(sa[0][i], sa[0][i], 1, 1);
+        av[i] = decode8_f16(w, sc);
       }
+    };
+    auto read_b = [&](int st, f16x8 (&bv)[FN]) {
+      const uint8_t *bb = lds_cur + BM * RB;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        cb[0][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch0);
-        cb[1][j] = *reinterpret_cast<const uint4 *>(base + offB + j * 32 * RB + ch1);
-        uint32_t s4 = *reinterpret_cast<const uint32_t *>(base + soffB + j * 32 * SB);
-        if (!kFull) s4 &= smask;
-        sbv[0][j] = e4m3x2_to_f16<false>(s4);
-        sbv[1][j] = e4m3x2_to_f16<true>(s4);
+        const int row = wn * FN * 32 + j * 32 + l32;
+        bv[j] = *reinterpret_cast<const f16x8 *>(bb + row * Cfg::kRowBytesB + (((4 * h + st) ^ (l32 & 7)) << 4));
       }
     };
     auto decode = [&](int t, f16x8 (&av)[FM], f16x8 (&bv)[FN]) {
       const int sub = t >> 2, st = t & 3;
+      if constexpr (WF) {
+        decode_a(st, av);
+        read_b(st, bv);
+      } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint32_t w = st == 0 ? ca[sub][i].x : st == 1 ? ca[sub][i].y : st == 2 ? ca[sub][i].z : ca[sub][i].w;
-        const f16x2 sc = st < 2 ? __builtin_shufflevector(sa[sub][i], sa[sub][i], 0, 0)
-                                : __builtin_shufflevector(sa[sub][i], sa[sub][i], 1, 1);
-        av[i] = decode8_f16(w, sc);
-      }
+        for (int i = 0; i < FM; ++i) {
+          const uint32_t w = st == 0 ? ca[sub][i].x : st == 1 ? ca[sub][i].y : st == 2 ? ca[sub][i].z : ca[sub][i].w;
+          const f16x2 sc = st < 2 ? __builtin_shufflevector(sa[sub][i], sa[sub][i], 0, 0)
+                                  : __builtin_shufflevector(sa[sub][i], sa[sub][i], 1, 1);
+          av[i] = decode8_f16(w, sc);
+        }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t w = st == 0 ? cb[sub][j].x : st == 1 ? cb[sub][j].y : st == 2 ? cb[sub][j].z : cb[sub][j].w;
-        const f16x2 sc = st < 2 ? __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 0, 0)
-                                : __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 1, 1);
-        bv[j] = decode8_f16(w, sc);
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t w = st == 0 ? cb[sub][j].x : st == 1 ? cb[sub][j].y : st == 2 ? cb[sub][j].z : cb[sub][j].w;
+          const f16x2 sc = st < 2 ? __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 0, 0)
+                                  : __builtin_shufflevector(sbv[sub][j], sbv[sub][j], 1, 1);
+          bv[j] = decode8_f16(w, sc);
+        }
       }
     };
     auto mfmas = [&](const f16x8 (&av)[FM], const f16x8 (&bv)[FN]) {
@@ -582,31 +662,77 @@ void k_gemm(GemmArgs g) {
         block_barrier();
         if (kt + S - 1 < nk) issue(kt + S - 1, bufp((B + S - 1) % S));
         const uint8_t *base = bufp(B);
+        lds_cur = base;
         if constexpr (BF) {
           bf16_stage(base, kt);
         } else {
           const int64_t k0 = kb0 + (int64_t)kt * BK;
-          if (k0 >= job.k_lo && k0 + BK <= job.k_hi) lds_read(base, kt, std::true_type{});
+          if (WF || (k0 >= job.k_lo && k0 + BK <= job.k_hi)) lds_read(base, kt, std::true_type{});
           else lds_read(base, kt, std::false_type{});
+          if constexpr (WF) {
+            // FP16 B: step t+1's B fragments are read into a second set of registers
+            // before step t's MFMAs are issued
+            f16x8 av[FM], bv[FN], bn[FN];
+            decode(0, av, bv);
 #pragma unroll
-          for (int t = 0; t < kSteps; ++t) {
-            f16x8 av[FM], bv[FN];
-            decode(t, av, bv);
-            mfmas(av, bv);
+            for (int t = 0; t < kSteps; ++t) {
+              if (t + 1 < kSteps) read_b(t + 1, bn);
+              mfmas(av, bv);
+              if (t + 1 < kSteps) {
+                decode_a(t + 1, av);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bv[j] = bn[j];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < kSteps; ++t) {
+              f16x8 av[FM], bv[FN];
+              decode(t, av, bv);
+              mfmas(av, bv);
+            }
           }
           // Instruction order of the stage: the first step's decode, then every MFMA
           // followed by an even share of the later steps' decode, so that a wave
           // decodes the next step while its own MFMAs run (the compiler otherwise
           // groups each step's MFMAs after its whole decode).
-          constexpr int kMf = kSteps * FM * FN, kDec = (FM + FN) * 8;
-          constexpr int kPer = (kDec * (kSteps - 1) + kMf - 1) / kMf;
-          __builtin_amdgcn_sched_group_barrier(0x002, kDec, 0);  // VALU
+          constexpr int kMf = kSteps * FM * FN, kDec = (WF ? FM : FM + FN) * 8;  // decode VALU per step
+          if constexpr (WF) {
+            // FP16 B: the stage's A reads and step 0's B reads, step 0's decode; then per
+            // step its MFMAs, the next step's B reads right after the first of them and
+            // the next step's decode spread over the rest
+            constexpr int kMs = FM * FN, kPerW = (kDec + kMs - 2) / (kMs - 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM + FN, 0);  // DS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, kDec, 0);         // VALU
 #pragma unroll
-          for (int i = 0; i < kMf; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);  // VALU
+            for (int t = 0; t < kSteps; ++t) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if (t + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, FN, 0);
+#pragma unroll
+              for (int i = 1; i < kMs; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (t + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x002, kPerW, 0);
+              }
+            }
+          } else {
+            constexpr int kPer = (kDec * (kSteps - 1) + kMf - 1) / kMf;
+            __builtin_amdgcn_sched_group_barrier(0x002, kDec, 0);  // VALU
+#pragma unroll
+            for (int i = 0; i < kMf; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, kPer, 0);  // VALU
+            }
           }
         }
+      };
+      // KSPLIT: the first K half's accumulators times G[2e] / G[2e+1]
+      auto rescale = [&]() {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] *= k_ratio;
       };
       if constexpr (S == 2) {
         // pairs of stages with no branch between them, then the odd stage: with a
@@ -615,14 +741,6 @@ void k_gemm(GemmArgs g) {
         // accumulators once, before the first stage of the second K half (a uniform
         // branch, so that the loop body exists once).
         const int nks = KSPLIT ? (int)((K >> 1) / BK) : -1;  // first stage of the second K half
-        auto rescale = [&]() {
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] *= k_ratio;
-        };
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
           if (KSPLIT && kt == nks) rescale();
@@ -635,11 +753,15 @@ void k_gemm(GemmArgs g) {
           stage(0, kt);
         }
       } else {
-        static_assert(!KSPLIT, "the K-half rescale is built for the two-stage ring");
+        const int nks = KSPLIT ? (int)((K >> 1) / BK) : -1;  // first stage of the second K half
         for (int kt = 0; kt < nk; kt += S) {
+          if (KSPLIT && kt == nks) rescale();
           stage(0, kt);
+          if (KSPLIT && kt + 1 == nks) rescale();
           if (kt + 1 < nk) stage(1, kt + 1);
+          if (KSPLIT && S > 2 && kt + 2 == nks) rescale();
           if (S > 2 && kt + 2 < nk) stage(2 % S, kt + 2);
+          if (KSPLIT && S > 3 && kt + 3 == nks) rescale();
           if (S > 3 && kt + 3 < nk) stage(3 % S, kt + 3);
         }
       }
@@ -748,6 +870,11 @@ using GemmTileK = GemmTile;
 // them for 256 compute units): 128 x 256 workgroup tiles of eight 64 x 64 wave tiles,
 // twice the tiles at 8 instead of 6 decode instructions per MFMA.
 using GemmTileSmall = TileCfg<2, 4, 2, 2, 2, 2>;
+// NVFP4 A, exact FP16 B (decoded weights): 256 x 256 workgroup tiles of eight 64 x 128
+// wave tiles (two A fragments decoded per eight MFMAs, B read from LDS as it is),
+// stages of 64 (41 KB: 256 A rows of 32 code and 4 scale bytes, 256 B rows of 128
+// bytes), double buffered.
+using GemmTileWf16 = TileCfg<4, 2, 2, 4, 2, 2, false, true>;
 // BF16 operands: 128 x 256 workgroup tiles of four 64 x 128 wave tiles, two
 // workgroups per CU, double-buffered 24 KB stages.  (Measured on the learner
 // batch: 15-25 % faster than 256 x 256 tiles with one workgroup per CU, whether

@@ -80,6 +80,7 @@ struct GemmArgs {
   int64_t ldc;
   float *amax_out;
   int operands_bf16;             // 1: a_codes / b_codes hold BF16 elements (no scales)
+  const uint16_t *b_f16;         // GROUP_M: B as exact FP16 values [b_rows][K] (no decode), or null
   int32_t *tile_counter;         // GROUP_K: workspace word for the dynamic tile schedule, or null
 };
 hipError_t launch_grouped_gemm(const GemmArgs &a, hipStream_t stream);
@@ -106,6 +107,9 @@ struct ConvertArgs {
   int64_t out_rows, out_cols;
 };
 hipError_t launch_convert(const ConvertArgs &a, hipStream_t stream);
+// exact FP16 values e2m1 * e4m3 of an NVFP4 tensor [rows][K] into out [rows][ldo]
+hipError_t launch_decode_f16(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K, uint16_t *out,
+                             int64_t ldo, hipStream_t stream);
 
 // ---------------------------------------------------------------- combine
 struct CombineArgs {

@@ -41,7 +41,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "nvfp4_grouped_gemm_workspace", "nvfp4_grouped_gemm", "moe_combine",
                           "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr",
                           "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma", "nv4_bench_mix",
-                          "moe_permute_noalloc", "moe_permute_noalloc_max_workspace", "nv4_amax"}
+                          "moe_permute_noalloc", "moe_permute_noalloc_max_workspace", "nv4_amax",
+                          "nvfp4_decode_f16"}
 
 
 def test_binding_covers_every_symbol():
@@ -174,6 +175,20 @@ def test_to_bf16_validation(lib):
     assert c(layout=3, nseg=2, ri=P, orow=256, ocol=32) == -3             # no gather when batched
     assert c(layout=9) == -1
     assert b"layout" in lib.nv4_last_error()
+
+
+def test_decode_f16_validation(lib):
+    P = ctypes.c_void_p(0x1000)
+    q = lambda rows=64, K=128, codes=0x1000: nv4.NV4Tensor(codes, 0x1000, 0x1000, rows, K, 0, 1)
+    d = lambda t, out=P, ldo=128: lib.nvfp4_decode_f16(ctypes.byref(t), out, ldo, None)
+    assert lib.nvfp4_decode_f16(None, P, 128, None) == -1      # no tensor
+    assert d(q(K=120), ldo=120) == -2                           # K % 16
+    assert d(q(), ldo=100) == -2                                # ldo < K
+    assert d(q(), ldo=132) == -2                                # ldo % 8
+    assert d(q(), out=ctypes.c_void_p(0x1008)) == -2            # out misaligned
+    assert d(q(codes=0x1004)) == -2                             # codes misaligned
+    assert d(q(), out=None) == -1                               # no output
+    assert d(q(rows=0), out=None) == 0                          # nothing to decode
 
 
 def test_bf16_gemm_validation(lib):
