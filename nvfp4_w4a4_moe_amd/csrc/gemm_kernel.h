@@ -738,15 +738,28 @@ void k_gemm(GemmArgs g) {
         // pairs of stages with no branch between them, then the odd stage: with a
         // conditional second stage the accumulators were copied between registers
         // on every iteration.  Stage kt is in buffer kt % 2.  KSPLIT rescales the
-        // accumulators once, before the first stage of the second K half (a uniform
-        // branch, so that the loop body exists once).
+        // accumulators once, before the first stage of the second K half.
         const int nks = KSPLIT ? (int)((K >> 1) / BK) : -1;  // first stage of the second K half
         int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-          if (KSPLIT && kt == nks) rescale();
-          stage(0, kt);
-          if (KSPLIT && kt + 1 == nks) rescale();
-          stage(1, kt + 1);
+        if (KSPLIT && (nks & 1) == 0) {
+          // the K halves meet between two pairs of stages: one loop over each half's
+          // pairs, the rescale between them (1-2 % faster than a test in the loop)
+          for (; kt < nks; kt += 2) {
+            stage(0, kt);
+            stage(1, kt + 1);
+          }
+          rescale();
+          for (; kt + 1 < nk; kt += 2) {
+            stage(0, kt);
+            stage(1, kt + 1);
+          }
+        } else {
+          for (; kt + 1 < nk; kt += 2) {
+            if (KSPLIT && kt == nks) rescale();
+            stage(0, kt);
+            if (KSPLIT && kt + 1 == nks) rescale();
+            stage(1, kt + 1);
+          }
         }
         if (kt < nk) {
           if (KSPLIT && kt == nks) rescale();
