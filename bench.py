@@ -224,8 +224,9 @@ def stats(ms: list) -> dict:
 def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
     """What plain kernels reach on this device (include/nv4moe_bench.h): a 16-byte
     non-temporal stream copy of 1 GiB (2 GiB of traffic), a read-only stream of 2 GiB,
-    and a loop of FP16 32x32x16 MFMAs with one and two waves per SIMD.  Median, min and
-    max over `reps` event-timed calls; the rate is reported at the median."""
+    a 4:1 read:write stream, 16-byte LDS reads on every CU, and a loop of FP16 32x32x16
+    MFMAs with one and two waves per SIMD.  Median, min and max over `reps` event-timed
+    calls; the rate is reported at the median."""
     st = torch.cuda.current_stream()
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -252,6 +253,11 @@ def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
     res["mix_4_1"] = m
     del quarter
     del src, dst, big
+    lo, nb = nv4.nv4_bench_lds(None, 4096)
+    m = stats(timed_events(torch, lambda: nv4.nv4_bench_lds(lo, 4096), max(5, reps // 4), st))
+    m["bytes_per_ns_per_cu"] = round(nb / (m["median_ms"] * 1e6) / torch.cuda.get_device_properties(0).multi_processor_count, 1)
+    m["kernel"] = "k_lds_read (16-byte reads, two 4-wave workgroups per CU)"
+    res["lds_read"] = m
     out = None
     for w in (1, 2):
         out, fl = nv4.nv4_bench_mfma(out, 4096, w)

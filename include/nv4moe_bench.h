@@ -47,6 +47,14 @@ nv4_status nv4_bench_mix(const void *src, size_t bytes, void *dst, void *stream)
 size_t nv4_bench_mfma_out_floats(int waves_per_simd);
 nv4_status nv4_bench_mfma(float *out, int iters, int waves_per_simd, void *stream);
 
+/* Two workgroups of 256 threads per compute unit, each filling a 64 KB LDS buffer and
+ * then reading it `iters` x 8 times per lane with 16-byte reads (every wave reads
+ * 1 KB of consecutive bytes per instruction, so no bank conflicts).  `out` receives
+ * one word per thread: nv4_bench_lds_out_words() of them.  LDS bytes read per call:
+ * nv4_bench_lds_out_words() * iters * 8 * 16. */
+size_t nv4_bench_lds_out_words(void);
+nv4_status nv4_bench_lds(uint32_t *out, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,8 @@ _SIGS = {
     "nv4_bench_copy": (_I, [_P, _P, _SZ, _P]),
     "nv4_bench_read": (_I, [_P, _SZ, ctypes.c_uint32, _P, _P]),
     "nv4_bench_mix": (_I, [_P, _SZ, _P, _P]),
+    "nv4_bench_lds_out_words": (_SZ, []),
+    "nv4_bench_lds": (_I, [_P, _I, _P]),
     "nv4_bench_mfma_out_floats": (_SZ, [_I]),
     "nv4_bench_mfma": (_I, [_P, _I, _I, _P]),
 }
@@ -900,3 +902,13 @@ def nv4_bench_mfma(out: torch.Tensor | None, iters: int, waves_per_simd: int = 2
         out = torch.empty(n, dtype=torch.float32, device="cuda")
     _check(lib.nv4_bench_mfma(_ptr(out), iters, waves_per_simd, _stream(stream)))
     return out, (n // 64) * iters * 8 * 32768
+
+
+def nv4_bench_lds(out: torch.Tensor | None, iters: int, stream=None) -> tuple:
+    """16-byte LDS reads on every compute unit; returns (out, LDS bytes read by the call)."""
+    lib = load()
+    n = lib.nv4_bench_lds_out_words()
+    if out is None or out.numel() < n:
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+    _check(lib.nv4_bench_lds(_ptr(out), iters, _stream(stream)))
+    return out, n * iters * 8 * 16

@@ -13,6 +13,9 @@
 //   k_stream_mix   4 reads of 16 bytes per 16-byte write, a quantiser's read:write mix.
 //   k_mfma_loop    eight independent v_mfma_f32_32x32x16_f16 chains per wave with no
 //                  memory traffic: the matrix-core issue rate at a given occupancy.
+//   k_lds_read     16-byte LDS reads of a 64 KB buffer, every wave reading 1 KB per
+//                  instruction (no bank conflicts), two workgroups of four waves per CU:
+//                  the LDS read bandwidth a compute unit delivers.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -106,6 +109,26 @@ void k_mfma_loop(float *out, int iters) {
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+constexpr int kLdsBytes = 65536;
+
+__global__ __launch_bounds__(256) void k_lds_read(uint32_t *out, int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kLdsBytes];
+  const int t = threadIdx.x;
+  for (int i = t; i < kLdsBytes / 16; i += 256) reinterpret_cast<u32x4 *>(buf)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = {0, 0, 0, 0};
+  const int base = t * 16;  // < 4096: a wave's 64 lanes read 1 KB of consecutive bytes
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int off = (base + ((it * 8 + u) & 15) * 4096) & (kLdsBytes - 1);  // 16-byte aligned, inside buf
+      acc += *reinterpret_cast<const u32x4 *>(buf + off);
+    }
+    asm volatile("" : "+v"(acc));  // keeps every read: the sum is not folded across iterations
+  }
+  out[(int64_t)blockIdx.x * 256 + t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 int stream_grid(int64_t n) {
   const int64_t want = (n + (int64_t)kStreamThreads * kStreamUnroll - 1) / ((int64_t)kStreamThreads * kStreamUnroll);
   return (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)device_cu_count() * 16));
@@ -146,6 +169,14 @@ nv4_status nv4_bench_mix(const void *src, size_t bytes, void *dst, void *stream)
                                                                (int64_t)nv4::device_cu_count() * 16));
   nv4::k_stream_mix<<<grid, nv4::kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const nv4::u32x4 *>(src), static_cast<nv4::u32x4 *>(dst), n);
+  return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
+}
+
+size_t nv4_bench_lds_out_words(void) { return (size_t)nv4::device_cu_count() * 2 * 256; }
+
+nv4_status nv4_bench_lds(uint32_t *out, int iters, void *stream) {
+  if (!out || iters <= 0) return NV4_EINVAL;
+  nv4::k_lds_read<<<nv4::device_cu_count() * 2, 256, 0, static_cast<hipStream_t>(stream)>>>(out, iters);
   return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
 }
 
