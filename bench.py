@@ -224,9 +224,9 @@ def stats(ms: list) -> dict:
 def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
     """What plain kernels reach on this device (include/nv4moe_bench.h): a 16-byte
     non-temporal stream copy of 1 GiB (2 GiB of traffic), a read-only stream of 2 GiB,
-    a 4:1 read:write stream, 16-byte LDS reads on every CU, and a loop of FP16 32x32x16
-    MFMAs with one and two waves per SIMD.  Median, min and max over `reps` event-timed
-    calls; the rate is reported at the median."""
+    a write-only stream of 2 GiB, a 4:1 read:write stream, 16-byte LDS reads on every
+    CU, and a loop of FP16 32x32x16 MFMAs with one and two waves per SIMD.  Median, min
+    and max over `reps` event-timed calls; the rate is reported at the median."""
     st = torch.cuda.current_stream()
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -245,6 +245,11 @@ def measure_ceilings(nv4, torch, reps: int = 20) -> dict:
     r["gbs"] = round(2 * n / (r["median_ms"] * 1e-3) / 1e9, 1)
     r["kernel"] = "k_stream_read"
     res["read"] = r
+    nv4.nv4_bench_write(big)
+    w = stats(timed_events(torch, lambda: nv4.nv4_bench_write(big), reps, st))
+    w["gbs"] = round(2 * n / (w["median_ms"] * 1e-3) / 1e9, 1)
+    w["kernel"] = "k_stream_write"
+    res["write"] = w
     quarter = torch.empty(2 * n // 16, dtype=torch.float32, device="cuda")
     nv4.nv4_bench_mix(big, quarter)
     m = stats(timed_events(torch, lambda: nv4.nv4_bench_mix(big, quarter), reps, st))

@@ -34,6 +34,10 @@ nv4_status nv4_bench_copy(const void *src, void *dst, size_t bytes, void *stream
  * caller that passes a value the data cannot produce gets a pure read stream. */
 nv4_status nv4_bench_read(const void *src, size_t bytes, uint32_t never, uint32_t *sink, void *stream);
 
+/* Write `bytes` (a positive multiple of 16) of dst with 16-byte ordinary stores, dst
+ * 16-byte aligned: `bytes` of HBM write traffic. */
+nv4_status nv4_bench_write(void *dst, size_t bytes, void *stream);
+
 /* Read `bytes` (a positive multiple of 4096) of src and write bytes / 4 to dst, a
  * quantiser's 4:1 read:write mix (BF16 in, FP4 codes out), with 16-byte non-temporal
  * loads and stores: 1.25 * bytes of HBM traffic. */

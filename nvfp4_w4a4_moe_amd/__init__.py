@@ -88,6 +88,7 @@ _SIGS = {
     "nv4_bench_copy": (_I, [_P, _P, _SZ, _P]),
     "nv4_bench_read": (_I, [_P, _SZ, ctypes.c_uint32, _P, _P]),
     "nv4_bench_mix": (_I, [_P, _SZ, _P, _P]),
+    "nv4_bench_write": (_I, [_P, _SZ, _P]),
     "nv4_bench_lds_out_words": (_SZ, []),
     "nv4_bench_lds": (_I, [_P, _I, _P]),
     "nv4_bench_mfma_out_floats": (_SZ, [_I]),
@@ -902,6 +903,11 @@ def nv4_bench_mfma(out: torch.Tensor | None, iters: int, waves_per_simd: int = 2
         out = torch.empty(n, dtype=torch.float32, device="cuda")
     _check(lib.nv4_bench_mfma(_ptr(out), iters, waves_per_simd, _stream(stream)))
     return out, (n // 64) * iters * 8 * 32768
+
+
+def nv4_bench_write(dst: torch.Tensor, stream=None) -> None:
+    """Fill dst (16-byte multiple) with 16-byte stores."""
+    _check(load().nv4_bench_write(_ptr(dst), dst.numel() * dst.element_size(), _stream(stream)))
 
 
 def nv4_bench_lds(out: torch.Tensor | None, iters: int, stream=None) -> tuple:

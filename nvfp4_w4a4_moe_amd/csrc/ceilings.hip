@@ -11,6 +11,8 @@
 //                  when it equals a value the caller never passes, so nothing is
 //                  written in practice and the loads cannot be removed.
 //   k_stream_mix   4 reads of 16 bytes per 16-byte write, a quantiser's read:write mix.
+//   k_stream_write 16-byte stores only (ordinary, write-back: a little faster here than
+//                  non-temporal ones), the bound of an output-heavy kernel.
 //   k_mfma_loop    eight independent v_mfma_f32_32x32x16_f16 chains per wave with no
 //                  memory traffic: the matrix-core issue rate at a given occupancy.
 //   k_lds_read     16-byte LDS reads of a 64 KB buffer, every wave reading 1 KB per
@@ -60,6 +62,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const u32x4 *__r
   for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == never) sink[0] = x;
+}
+
+__global__ __launch_bounds__(kStreamThreads) void k_stream_write(u32x4 *__restrict__ dst, int64_t n, uint32_t v) {
+  const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+  const u32x4 w = {v, v ^ 1u, v ^ 2u, (uint32_t)threadIdx.x};
+  for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride) dst[i] = w;
 }
 
 // Reads 4 x 16 bytes and writes 16 bytes per lane per round: the 4:1 read:write mix of
@@ -158,6 +166,17 @@ nv4_status nv4_bench_read(const void *src, size_t bytes, uint32_t never, uint32_
   const int64_t n = (int64_t)(bytes / 16);
   nv4::k_stream_read<<<nv4::stream_grid(n), nv4::kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const nv4::u32x4 *>(src), n, never, sink);
+  return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
+}
+
+nv4_status nv4_bench_write(void *dst, size_t bytes, void *stream) {
+  if (!dst || bytes == 0 || bytes % 16) return NV4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(dst) % 16) return NV4_EALIGN;
+  const int64_t n = (int64_t)(bytes / 16);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + nv4::kStreamThreads - 1) / nv4::kStreamThreads,
+                                                               (int64_t)nv4::device_cu_count() * 8));
+  nv4::k_stream_write<<<grid, nv4::kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<nv4::u32x4 *>(dst), n, 0x3F800000u);
   return hipGetLastError() == hipSuccess ? NV4_OK : NV4_EHIP;
 }
 

@@ -42,7 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "nv4_to_bf16", "bf16_grouped_gemm", "nvfp4_quantize_sr",
                           "nv4_bench_copy", "nv4_bench_read", "nv4_bench_mfma_out_floats", "nv4_bench_mfma", "nv4_bench_mix",
                           "moe_permute_noalloc", "moe_permute_noalloc_max_workspace", "nv4_amax",
-                          "nvfp4_decode_f16", "nv4_bench_lds", "nv4_bench_lds_out_words"}
+                          "nvfp4_decode_f16", "nv4_bench_lds", "nv4_bench_lds_out_words",
+                          "nv4_bench_write"}
 
 
 def test_binding_covers_every_symbol():
