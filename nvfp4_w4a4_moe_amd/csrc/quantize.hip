@@ -70,15 +70,26 @@ struct Chunk {
   uint4 w[F32 ? 2 : 1];
 };
 
-template <bool F32>
+// 16 bytes by a non-temporal load (the source is streamed once)
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const void *p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// NT: non-temporal loads, for sources read once (measured on the learner batch: the X
+// quantisation 19 % faster, the rows-and-columns passes 2-6 %); a gathered source
+// whose rows repeat keeps ordinary loads, which let the repeats hit in the caches.
+template <bool F32, bool NT = true>
 __device__ __forceinline__ Chunk<F32> load_chunk(const void *x, int64_t off) {
   Chunk<F32> c;
   if (F32) {
     const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + off);
-    c.w[0] = p[0];
-    c.w[F32 ? 1 : 0] = p[1];
+    c.w[0] = NT ? ld16_nt(p) : p[0];
+    c.w[F32 ? 1 : 0] = NT ? ld16_nt(p + 1) : p[1];
   } else {
-    c.w[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+    c.w[0] = NT ? ld16_nt(p) : *p;
   }
   return c;
 }
@@ -520,7 +531,7 @@ constexpr int kSegLds = 256;       // segment offsets staged in LDS up to this m
 constexpr int kOutPitch = 72;       // LDS out-tile row pitch for 64 code bytes (+8 breaks bank aliasing)
 constexpr int kScalePitch = 12;
 
-template <bool F32, int P, int C, bool ROWS_TOO, bool SR>
+template <bool F32, int P, int C, bool ROWS_TOO, bool SR, bool NT = true>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles_per_seg, int gx, int64_t ntiles) {
   typedef typename std::conditional<F32, float, uint16_t>::type T;
   static_assert(P == 128, "tiles of 128 positions (8 blocks)");
@@ -650,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
     const int pp = i * kRowsPerPass + lr;
     const int j = pp >> 4, r = pp & 15;
     v[i] = Chunk<F32>{};
-    if (col_ok && r < bnum[j]) v[i] = load_chunk<F32>(a.x, row_off(a, bsrc[j] + r) + c0 + lch * 8);
+    if (col_ok && r < bnum[j]) v[i] = load_chunk<F32, NT>(a.x, row_off(a, bsrc[j] + r) + c0 + lch * 8);
   }
   // 2. row blocks of the tile's valid rows (tensor scale) from the loaded registers:
   // lanes 2m and 2m + 1 of a row hold the two halves of one 16-element block
@@ -861,6 +872,8 @@ hipError_t launch_quantize_t(const QuantArgs &a, hipStream_t stream) {
       else k_quant_cols<true, P, 64, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles, (int)gx, ntiles);
     } else {
       if (both) k_quant_cols<false, P, 128, true, SR><<<grid, kThreads, 0, stream>>>(a, ptiles, (int)gx, ntiles);
+      else if (a.row_index)  // gathered rows (X in expert order) repeat: ordinary loads
+        k_quant_cols<false, P, 64, false, SR, false><<<grid, kThreads, 0, stream>>>(a, ptiles, (int)gx, ntiles);
       else k_quant_cols<false, P, 64, false, SR><<<grid, kThreads, 0, stream>>>(a, ptiles, (int)gx, ntiles);
     }
   }
