@@ -332,15 +332,111 @@ void k_gemm(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot is written
     block_barrier();
   }
+  // ---- epilogue of a finished tile (job ej, column tile en, B scales eg / eu, row
+  // scales of iteration eit): tensor scales, optional SwiGLU, store
+  constexpr int NJ = EPI == NV4_EPI_SWIGLU ? FN / 2 : FN;
+  constexpr int ESZ = OUT_F32 ? 4 : 2;
+  f32x16 acc[FM][FN];
+  TileJob ej{};
+  int64_t en = 0;
+  float eg = 1.0f, eu = 1.0f;
+  auto epilogue = [&](int64_t eit) {
+    const int ldc = (int)g.ldc;
+    int colw, ncols;  // first output column of this wave's fragment 0 (before the lane), column count
+    if (EPI == NV4_EPI_SWIGLU) {
+      colw = (int)en * (BN / 2) + wn * (FN / 2 * 32);
+      ncols = (int)g.N;
+    } else if (GROUP == NV4_GROUP_M) {
+      colw = (int)en * BN + wn * FN * 32;
+      ncols = (int)g.N;
+    } else {
+      colw = (int)ej.n0 + wn * FN * 32;
+      ncols = (int)g.b_rows;
+    }
+    const int rows_valid = (int)std::min<int64_t>(ej.m_end - ej.m0, BM) - wm * FM * 32;
+    // this wave's rows start at tile row wm*FM*32; lane half h adds 4 rows
+    char *cw = static_cast<char *>(g.C) +
+               ((int64_t)(GROUP == NV4_GROUP_K ? ej.e * g.a_rows : 0) + ej.m0 + wm * FM * 32) * g.ldc * ESZ;
+    // lane offsets: row q (0..3) of a 4-row group plus 4 rows for lane half h, column
+    // of fragment j (an invalid column gets an offset past any buffer)
+    uint32_t voff[4][NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = colw + j * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        voff[q][j] = col < ncols ? (uint32_t)(((q + h * 4) * ldc + col) * ESZ) : 0x80000000u;
+    }
+    const float sc = a_ts * eg, sc_up = a_ts * eu;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ru = i * 32 + g4 * 8;  // first row of the group for lane half 0
+        // bytes from row ru to the end of the valid rows, at most 8 rows (the group's
+        // offsets stay below 8 rows)
+        const int left = std::min(std::max(rows_valid - ru, 0), 8);
+        char *rb = cw + (int64_t)ru * g.ldc * ESZ;
+        const uint32_t nb = (uint32_t)(left * ldc * ESZ);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = g4 * 4 + q;
+          float rsc = sc, rsc_up = sc_up;
+          if (A_ROW_SCALE) {
+            const float ra = row_scale[eit & 1][wm * FM * 32 + ru + q + h * 4];
+            rsc = ra * eg;
+            rsc_up = ra * eu;
+          }
+          if (EPI == NV4_EPI_SWIGLU) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const float gt = acc[i][j][r] * rsc;
+              const float up = acc[i][j + FN / 2][r] * rsc_up;
+              // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
+              const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+              float stored;
+              if (OUT_F32) {
+                store_row_b32(rb, nb, voff[q][j], hv);
+                stored = hv;
+              } else {
+                const uint16_t b16 = bf16_of(hv);
+                store_row_b16(rb, nb, voff[q][j], b16);
+                stored = bf16_bits_to_f32(b16);
+              }
+              // rows and columns outside the tile hold exact zeros (zero operands)
+              amax_run = fmaxf(amax_run, fabsf(stored));
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const float v = acc[i][j][r] * rsc;
+              if (OUT_F32) store_row_b32(rb, nb, voff[q][j], v);
+              else store_row_b16(rb, nb, voff[q][j], bf16_of(v));
+            }
+          }
+        }
+      }
+    }
+  };
+  // FP32 GROUP_M outputs (the down projection: K = I, six stages of 128 per tile, then
+  // 256 KB of stores) issue a tile's C stores in the next iteration, after the next
+  // tile's first LDS DMA, so that they drain while its first stage computes (GEMM2
+  // 4 % faster on the learner batch; the BF16-output GEMMs were 0.5-2.5 % slower that
+  // way and keep the stores at the end of the tile).
+  constexpr bool kLate = OUT_F32 && GROUP == NV4_GROUP_M;
+  constexpr int kEpiStores = FM * 16 * NJ;  // buffer stores every wave issues per tile
+  constexpr int kPostEpiWait = kEpiStores < 63 ? kEpiStores : 63;
   for (int64_t it = 0;; ++it) {
     const int64_t L = dyn ? (int64_t)__builtin_amdgcn_readfirstlane(scratch[it & 1])
                           : it * G + (int64_t)xcd * per_xcd + slot;
-    if (L >= total) break;
+    const bool have = L < total;  // uniform
+    if (!kLate && !have) break;
     int next_tile = 0;
-    if (dyn && tid == 0) next_tile = atomicAdd(g.tile_counter, 1);
-    TileJob job;
-    int64_t nt_idx;
-    if (GROUP == NV4_GROUP_M) {
+    if (have && dyn && tid == 0) next_tile = atomicAdd(g.tile_counter, 1);
+    TileJob job{};  // with no tile: an empty K range, no DMA, rows that load nothing
+    int64_t nt_idx = 0;
+    if (!have) {
+    } else if (GROUP == NV4_GROUP_M) {
       const int64_t mt = L / ntn;
       nt_idx = L - mt * ntn;
       int lo = 0, hi = E - 1;  // last expert with tstart[e] <= mt (it owns >= 1 tile)
@@ -485,14 +581,6 @@ void k_gemm(GemmArgs g) {
         b_gate = b_up = g.b_tscale[job.e];
       }
     }
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // LDS stage layout: a row holds the stage's 128 codes in four XOR-swizzled
     // 16-byte chunks and its 8 scale bytes.  Lane half h takes stage elements
@@ -656,9 +744,27 @@ void k_gemm(GemmArgs g) {
     // stage kt is computed); unrolled by S so that every buffer is a fixed LDS object.
     for (int s0 = 0; s0 < S - 1; ++s0)
       if (s0 < nk) issue(s0, bufp(s0));
+    if constexpr (kLate) {
+      // the previous tile's C stores follow this tile's first DMA in issue order
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (it > 0) epilogue(it - 1);
+      if (!have) break;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     {
       auto stage = [&](const int B, int kt) {  // B = kt % S, a literal at every call
-        wait_stage(std::min(S - 2, nk - 1 - kt));
+        // A wave's vector-memory operations retire in issue order (loads, LDS DMA and
+        // stores alike, one vmcnt).  With kLate, stage 0 of a tile after the first was
+        // issued before the previous tile's kEpiStores C stores: waiting until at most
+        // that many operations are outstanding leaves the stores in flight.
+        if (kLate && S == 2 && kt == 0 && it > 0) wait_vmcnt<kPostEpiWait>();
+        else wait_stage(std::min(S - 2, nk - 1 - kt));
         block_barrier();
         if (kt + S - 1 < nk) issue(kt + S - 1, bufp((B + S - 1) % S));
         const uint8_t *base = bufp(B);
@@ -784,85 +890,11 @@ void k_gemm(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     block_barrier();
 
-    // ---- epilogue: tensor scales, optional SwiGLU, store
-    const int ldc = (int)g.ldc;
-    int colw, ncols;  // first output column of this wave's fragment 0 (before the lane), column count
-    if (EPI == NV4_EPI_SWIGLU) {
-      colw = (int)nt_idx * (BN / 2) + wn * (FN / 2 * 32);
-      ncols = (int)g.N;
-    } else if (GROUP == NV4_GROUP_M) {
-      colw = (int)nt_idx * BN + wn * FN * 32;
-      ncols = (int)g.N;
-    } else {
-      colw = (int)job.n0 + wn * FN * 32;
-      ncols = (int)g.b_rows;
-    }
-    constexpr int ESZ = OUT_F32 ? 4 : 2;
-    constexpr int NJ = EPI == NV4_EPI_SWIGLU ? FN / 2 : FN;
-    const int rows_valid = (int)std::min<int64_t>(job.m_end - job.m0, BM) - wm * FM * 32;
-    // this wave's rows start at tile row wm*FM*32; lane half h adds 4 rows
-    char *cw = static_cast<char *>(g.C) +
-               ((int64_t)(GROUP == NV4_GROUP_K ? job.e * g.a_rows : 0) + job.m0 + wm * FM * 32) * g.ldc * ESZ;
-    // lane offsets: row q (0..3) of a 4-row group plus 4 rows for lane half h, column
-    // of fragment j (an invalid column gets an offset past any buffer)
-    uint32_t voff[4][NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = colw + j * 32 + l32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        voff[q][j] = col < ncols ? (uint32_t)(((q + h * 4) * ldc + col) * ESZ) : 0x80000000u;
-    }
-    const float sc = a_ts * b_gate, sc_up = a_ts * b_up;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int ru = i * 32 + g4 * 8;  // first row of the group for lane half 0
-        // bytes from row ru to the end of the valid rows, at most 8 rows (the group's
-        // offsets stay below 8 rows)
-        const int left = std::min(std::max(rows_valid - ru, 0), 8);
-        char *rb = cw + (int64_t)ru * g.ldc * ESZ;
-        const uint32_t nb = (uint32_t)(left * ldc * ESZ);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = g4 * 4 + q;
-          float rsc = sc, rsc_up = sc_up;
-          if (A_ROW_SCALE) {
-            const float ra = row_scale[it & 1][wm * FM * 32 + ru + q + h * 4];
-            rsc = ra * b_gate;
-            rsc_up = ra * b_up;
-          }
-          if (EPI == NV4_EPI_SWIGLU) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const float gt = acc[i][j][r] * rsc;
-              const float up = acc[i][j + FN / 2][r] * rsc_up;
-              // silu(g) * u with the hardware exp2 and reciprocal (relative error ~1e-7)
-              const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-              float stored;
-              if (OUT_F32) {
-                store_row_b32(rb, nb, voff[q][j], hv);
-                stored = hv;
-              } else {
-                const uint16_t b16 = bf16_of(hv);
-                store_row_b16(rb, nb, voff[q][j], b16);
-                stored = bf16_bits_to_f32(b16);
-              }
-              // rows and columns outside the tile hold exact zeros (zero operands)
-              amax_run = fmaxf(amax_run, fabsf(stored));
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const float v = acc[i][j][r] * rsc;
-              if (OUT_F32) store_row_b32(rb, nb, voff[q][j], v);
-              else store_row_b16(rb, nb, voff[q][j], bf16_of(v));
-            }
-          }
-        }
-      }
-    }
+    ej = job;
+    en = nt_idx;
+    eg = b_gate;
+    eu = b_up;
+    if constexpr (!kLate) epilogue(it);
   }
   if (EPI == NV4_EPI_SWIGLU && g.amax_out) {
     const float w = wave_max(amax_run);
