@@ -569,13 +569,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   // Tile t = by * gx + bx (column tile bx, position tile by).  Workgroup g runs on XCD
   // g % 8 (the hardware's round-robin).  Tiles write scale bytes in 8-byte pieces of
   // 64-byte lines (per output row and tile); pieces of one line merge in an XCD's L2
-  // before being written back only if they come from the same XCD.  With gx % 8 == 0
-  // tile t on workgroup t already puts the next position tile (t + gx) on the same XCD;
-  // otherwise the tiles are handed out in 8 contiguous chunks, one per XCD (measured:
-  // the rows-and-columns passes of the SwiGLU output and of dY13, gx = 6 and 12, 5 %
-  // faster; with gx % 8 == 0 the chunks were no faster).
+  // before being written back only if they come from the same XCD, close in time.
+  // Column scales: the next position tile (t + gx) holds the neighbouring pieces, and
+  // with gx % 8 == 0 tile t on workgroup t already puts it on the same XCD, four tiles
+  // later.  Row scales (NV4_ROWS_AND_COLS): the neighbouring pieces are in the other
+  // column tiles of the band (t + 1, ...).  So the tiles go to the XCDs in 8 contiguous
+  // chunks, one per XCD, for the rows-and-columns passes and whenever gx % 8 != 0
+  // (measured on the learner batch: the rows-and-columns pass of dY2, gx = 16, writes
+  // 1231 instead of 1412 MB for 1210 MB of output and runs 5 % faster, those of the
+  // SwiGLU output and dY13, gx = 6 and 12, 5 % faster; the column pass of the gathered
+  // X, gx = 32, writes 686 instead of 608 MB in chunks and runs 2 % slower).
   int64_t t = blockIdx.x;
-  if (gx % kXcdCount) {
+  if (ROWS_TOO || gx % kXcdCount) {
     const int64_t chunk = (ntiles + kXcdCount - 1) / kXcdCount;
     t = (int64_t)(blockIdx.x % kXcdCount) * chunk + blockIdx.x / kXcdCount;
   }
