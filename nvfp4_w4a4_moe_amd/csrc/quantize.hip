@@ -577,15 +577,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantArgs a, int ptiles
   // chunks, one per XCD, for the rows-and-columns passes and whenever gx % 8 != 0
   // (measured on the learner batch: the rows-and-columns pass of dY2, gx = 16, writes
   // 1231 instead of 1412 MB for 1210 MB of output and runs 5 % faster, those of the
-  // SwiGLU output and dY13, gx = 6 and 12, 5 % faster; the column pass of the gathered
-  // X, gx = 32, writes 686 instead of 608 MB in chunks and runs 2 % slower).
+  // SwiGLU output and dY13, gx = 6 and 12, 5 % faster).
+  // Gathered rows (X in expert order, each token's row in k segments): the tiles are
+  // taken column tile by column tile (t = bx * gy + by), so that the k repeats of a
+  // row's C columns fall within one column tile's pass over the positions and are
+  // read from the caches (the 64-column slab of the learner batch's X is 8 MB); in
+  // chunks, so that position-neighbours stay on one XCD (0.64 -> 0.56 ms; the
+  // position-major order in chunks was 2 % slower than in the plain order).
   int64_t t = blockIdx.x;
-  if (ROWS_TOO || gx % kXcdCount) {
+  const bool gathered = !ROWS_TOO && a.row_index != nullptr;
+  if (gathered || ROWS_TOO || gx % kXcdCount) {
     const int64_t chunk = (ntiles + kXcdCount - 1) / kXcdCount;
     t = (int64_t)(blockIdx.x % kXcdCount) * chunk + blockIdx.x / kXcdCount;
   }
   if (t >= ntiles) return;  // uniform over the workgroup
-  const int64_t bx = t % gx, by = t / gx;
+  const int64_t gy = ntiles / gx;  // position tiles
+  const int64_t bx = gathered ? t / gy : t % gx, by = gathered ? t % gy : t / gx;
   if (blockIdx.x == 0) write_group_scales(a);
   const float *A = amax_src(a);
   const int64_t Ccols = a.K;  // columns of x
