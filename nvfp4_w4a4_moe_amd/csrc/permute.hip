@@ -62,7 +62,9 @@ __device__ __forceinline__ int wave_min_dpp(int v) {
 // statistics, then k rounds of a wave-wide argmax.  Each round: every lane's best
 // untaken candidate (larger logit first, then lower id), the wave's maximum value,
 // and among the lanes holding it the lowest id (a ballot; a second reduction only
-// when several lanes tie).
+// when several lanes tie).  Lane j keeps round j's id and logit; the k softmax
+// weights are formed after the rounds, one per lane (the kernel is bound by its VALU
+// work: an exp and a division in every round cost a third of it).
 template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
   const int lane = threadIdx.x & 63;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
   s = wave_sum_dpp(s);
   uint32_t taken = 0;
   int my_id = 0;
-  float my_w = 0.0f, wsum = 0.0f;
+  float my_v = -INFINITY;
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
@@ -114,11 +116,11 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
       wid = wave_min_dpp(((cand >> lane) & 1) ? bi : 0x7FFFFFFF);
     }
     if (wid < E && (wid & 63) == lane) taken |= 1u << (wid >> 6);
-    const float w = expf(vmax - mx) / s;
-    wsum += w;
-    if (lane == j) { my_id = wid; my_w = w; }
+    if (lane == j) { my_id = wid; my_v = vmax; }
   }
-  if (a.flags & NV4_RENORM) my_w = my_w / wsum;
+  float my_w = 0.0f;
+  if (lane < a.k) my_w = expf(my_v - mx) / s;
+  if (a.flags & NV4_RENORM) my_w = my_w / wave_sum_dpp(my_w);  // lanes >= k hold 0
   if (lane < a.k) {
     a.topk_ids[t * a.k + lane] = my_id;
     a.topk_w[t * a.k + lane] = my_w;
