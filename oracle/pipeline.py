@@ -34,11 +34,11 @@ expert outputs as FP32), so these functions give an end-to-end oracle result.
 Pins: the single-expert top-1 forward equals a dense W4A4 SwiGLU MLP, and every
 gradient of ``moe_backward`` is the adjoint of its forward GEMM on the backward's
 own dequantised operands (tests/test_oracle_moe.py, tests/test_oracle_backward.py).
-Parity unpinned: the end-to-end agreement of the GPU pipeline with this one.
-After an intermediate tensor is re-quantised, an FP32-vs-FP64 accumulation
-difference upstream can move an element across an FP4 rounding boundary, so the
-two pipelines agree only statistically; the GPU tests pin every stage separately
-instead, each fed the GPU's own stage inputs.
+End to end, the GPU pipeline agrees with this one only statistically: after an
+intermediate tensor is re-quantised, an FP32-vs-FP64 accumulation difference
+upstream can move an element across an FP4 rounding boundary.  The GPU tests
+therefore compare every stage separately, each fed the GPU's own stage inputs, and
+the whole layer only loosely.
 """
 
 from __future__ import annotations
