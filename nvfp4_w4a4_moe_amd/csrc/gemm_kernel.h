@@ -897,8 +897,18 @@ void k_gemm(GemmArgs g) {
     if constexpr (!kLate) epilogue(it);
   }
   if (EPI == NV4_EPI_SWIGLU && g.amax_out) {
+    // one atomic per workgroup: the waves' maxima meet in LDS first (same-address
+    // atomics serialise in L2, and every workgroup ends at about the same time)
+    __shared__ float wave_amax[NW];
     const float w = wave_max(amax_run);
-    if (lane == 0) atomic_max_nonneg(g.amax_out, w);
+    if (lane == 0) wave_amax[wave] = w;
+    __syncthreads();
+    if (tid == 0) {
+      float m = wave_amax[0];
+#pragma unroll
+      for (int i = 1; i < NW; ++i) m = fmaxf(m, wave_amax[i]);
+      atomic_max_nonneg(g.amax_out, m);
+    }
   }
 }
 
