@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
     a.topk_ids[t * a.k + lane] = my_id;
     a.topk_w[t * a.k + lane] = my_w;
   }
-  if (nan && lane == 0 && a.dev_status) atomicOr(a.dev_status, kDsNanLogit);
+  // any lane's NaN (each lane held only its own experts' logits)
+  if (__ballot(nan) != 0 && lane == 0 && a.dev_status) atomicOr(a.dev_status, kDsNanLogit);
 }
 
 // one wave per chunk: rank of each assignment among the chunk's assignments to

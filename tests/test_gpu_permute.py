@@ -74,6 +74,26 @@ def test_bad_expert_id_sets_status(gpu_lib):
     assert int(st.item()) & gpu_lib.NV4_DS_BAD_EXPERT
 
 
+def test_nan_logit_sets_status(gpu_lib):
+    """A NaN router logit is out of contract: the status word says so, the token's
+    selection skips the NaN (top-k of its finite logits, ties to the lower id), and
+    every other token is routed exactly as without it."""
+    T, E, k = 64, 16, 4
+    lg = synth.rng(11).standard_normal((T, E)).astype(np.float32)
+    bad = lg.copy()
+    bad[5, [2, 7]] = np.nan
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rt = gpu_lib.moe_permute(dev_f32(bad), E, k, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & gpu_lib.NV4_DS_NAN_LOGIT
+    ids_ref, _ = moe.route_topk(lg, k)
+    got = host(rt.topk_ids)
+    keep = np.arange(T) != 5
+    assert np.array_equal(got[keep], ids_ref[keep])
+    finite = np.where(np.isnan(bad[5]), -np.inf, bad[5])
+    assert list(got[5]) == list(np.argsort(-finite, kind="stable")[:k])
+
+
 def test_gather_rows_exact(gpu_lib):
     cfg = synth.CONFIGS["tiny"]
     x = synth.activations(cfg.T, cfg.H, cfg.seed)
