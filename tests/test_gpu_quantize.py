@@ -163,6 +163,33 @@ def test_nonfinite_sets_status(gpu_lib):
     assert int(st.item()) & gpu_lib.NV4_DS_NONFINITE
 
 
+@pytest.mark.parametrize("layout", ["rows", "cols", "rows_and_cols", "per_row"])
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_nonfinite_sets_status_without_amax_pass(gpu_lib, layout, bad):
+    """With the amax given (no amax pass), each quantisation kernel itself flags a NaN
+    or infinity, wherever it sits in the tile (here in a lane other than the first)."""
+    R, K = 300, 256
+    x = synth.to_bf16_values(synth.activations(R, K, 21))
+    x[137, 203] = bad
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    amax = torch.tensor([4.0], dtype=torch.float32, device="cuda")
+    xd = dev_bf16(x)
+    if layout == "rows":
+        gpu_lib.nvfp4_quantize(xd, amax_in=amax, dev_status=st)
+    elif layout == "per_row":
+        gpu_lib.nvfp4_quantize(xd, scale_mode=gpu_lib.NV4_SCALE_ROW, dev_status=st)
+    else:
+        off = torch.tensor([0, 120, R], dtype=torch.int32, device="cuda")
+        pad = torch.tensor([0, 128, 128 + 192], dtype=torch.int32, device="cuda")
+        kw = dict(nseg=2, seg_offsets=off, seg_padded_offsets=pad, amax_in=amax, dev_status=st)
+        if layout == "cols":
+            gpu_lib.nvfp4_quantize(xd, layout=gpu_lib.NV4_COLS, **kw)
+        else:
+            gpu_lib.nvfp4_quantize(xd, layout=gpu_lib.NV4_ROWS_AND_COLS, **kw)
+    torch.cuda.synchronize()
+    assert int(st.item()) & gpu_lib.NV4_DS_NONFINITE
+
+
 def test_columns_segmented(gpu_lib):
     """Transposed quantisation by expert segment, as the weight-gradient GEMMs use."""
     cfg = synth.CONFIGS["tiny"]
