@@ -190,6 +190,19 @@ def test_combine_tiny(gpu_lib):
     assert rel_frob(host(out_b), ref) <= TOL
 
 
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_combine_other_k(gpu_lib, k):
+    """The combine for k other than 8 (k = 3 and 5 take the kernel's run-time k loop),
+    H not a multiple of the workgroup's 1024 columns, FP32 and BF16 expert rows."""
+    T, E, H = 200, 12, 1344
+    lg = synth.rng(44 + k).standard_normal((T, E)).astype(np.float32)
+    rt = gpu_lib.moe_permute(dev_f32(lg), E, k)
+    Y = synth.activations(T * k, H, 45)
+    ref = moe.combine(Y, host(rt.token_row), host(rt.topk_w))
+    assert rel_frob(host(gpu_lib.moe_combine(dev_f32(Y), rt.token_row, rt.topk_w)), ref) <= TOL
+    assert rel_frob(host(gpu_lib.moe_combine(dev_bf16(Y), rt.token_row, rt.topk_w)), ref) <= TOL
+
+
 def test_combine_unpermute_exact(gpu_lib):
     cfg = synth.CONFIGS["tiny"]
     lg = synth.router_logits(cfg)

@@ -264,6 +264,27 @@ def test_rows_and_columns_with_row_gather(gpu_lib):
     _assert_exact(t.rows_out, Q.quantize_rows(xg))
 
 
+@pytest.mark.parametrize("C", [64, 320, 2048])
+def test_columns_with_row_gather(gpu_lib, C):
+    """NV4_COLS with the fused gather (X in expert order for the weight gradient): the
+    column output is the per-segment transposed quantisation of the gathered rows,
+    with several column tiles (taken column tile by column tile) and ragged, empty
+    and padded segments; the tensor scale is X's (amax_in)."""
+    T, R = 300, 900
+    x = synth.activations(T, C, 25)
+    idx = synth.rng(26).integers(0, T, R).astype(np.int32)
+    off = np.array([0, 17, 17, 400, 899, 900])
+    po = Q.padded_offsets(off)
+    amax = torch.tensor([np.abs(x).max()], dtype=torch.float32, device="cuda")
+    t = gpu_lib.nvfp4_quantize(dev_bf16(x), layout=gpu_lib.NV4_COLS, nseg=len(off) - 1, seg_offsets=dev_i32(off),
+                               seg_padded_offsets=dev_i32(po), row_index=dev_i32(idx), amax_in=amax)
+    xg = x[idx]
+    ref_c, _ = Q.quantize_cols(xg, off, amax=float(np.abs(x).max()))
+    Kp = int(po[-1])
+    assert np.array_equal(host(t.codes)[:, : Kp // 2], ref_c.packed())
+    assert np.array_equal(host(t.scales)[:, : Kp // 16], ref_c.scales)
+
+
 # ---------------------------------------------------------------- rounding edge cases
 # The bytes are decided by two round-to-nearest-even steps ("The 4-bitter Lesson",
 # section "Improving Gradient Stability", footnote 6: clip(round(w/s))): the E4M3
