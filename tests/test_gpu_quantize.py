@@ -374,7 +374,8 @@ def test_columns_with_segment_scales_exact(gpu_lib):
     assert len(set(ref.G.tolist())) >= 3
 
 
-@pytest.mark.parametrize("K,f32", [(4096, False), (4608, False), (784, True), (8192 + 16, True)])
+@pytest.mark.parametrize("K,f32", [(4096, False), (4608, False), (784, True), (8192 + 16, True), (2048, False),
+                                   (1040, True), (16, False)])
 def test_rows_per_token_long_and_fp32_rows(gpu_lib, K, f32):
     """NV4_SCALE_ROW with rows held in registers (K <= 4096) and rows read twice
     (longer), BF16 and FP32 input: bit-exact, per-row amaxes exact."""
