@@ -33,43 +33,54 @@ constexpr int kMaxE = 1024;
 // Wave-wide reductions over 64 lanes without LDS: DPP within rows of 16 lanes (the
 // pairs (i, i^1), (i, i^2), then the half-row and row mirrors), then the gfx950
 // row swaps across 16 and 32 lanes.  Every lane ends with the result.
-template <class F>
+template <int LANES = 64, class F>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
+  static_assert(LANES == 32 || LANES == 64, "reductions over 32-lane halves or the wave");
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
   const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   v = op(s16[0], s16[1]);
+  if (LANES == 32) return v;  // each 32-lane half holds its own result
   const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return op(s32[0], s32[1]);
 }
+template <int LANES = 64>
 __device__ __forceinline__ float wave_max_dpp(float v) {
-  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+  return __uint_as_float(wave_reduce_u32<LANES>(__float_as_uint(v), [](uint32_t x, uint32_t y) {
     return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
   }));
 }
+template <int LANES = 64>
 __device__ __forceinline__ float wave_sum_dpp(float v) {
-  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+  return __uint_as_float(wave_reduce_u32<LANES>(__float_as_uint(v), [](uint32_t x, uint32_t y) {
     return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
   }));
 }
+template <int LANES = 64>
 __device__ __forceinline__ int wave_min_dpp(int v) {
-  return (int)wave_reduce_u32((uint32_t)v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int)x, (int)y); });
+  return (int)wave_reduce_u32<LANES>((uint32_t)v, [](uint32_t x, uint32_t y) { return (uint32_t)min((int)x, (int)y); });
 }
 
-// One wave per token, NPL logits per lane (expert e = lane + 64 * i): softmax
-// statistics, then k rounds of a wave-wide argmax.  Each round: every lane's best
-// untaken candidate (larger logit first, then lower id), the wave's maximum value,
-// and among the lanes holding it the lowest id (a ballot; a second reduction only
-// when several lanes tie).  Lane j keeps round j's id and logit; the k softmax
-// weights are formed after the rounds, one per lane (the kernel is bound by its VALU
-// work: an exp and a division in every round cost a third of it).
-template <int NPL>
+// LPT lanes per token (64: one token per wave; 32: two, one per half-wave), NPL
+// logits per lane (expert e = lane-in-token + LPT * i): softmax statistics, then k
+// rounds of an argmax over the token's lanes.  Each round: every lane's best untaken
+// candidate (larger logit first, then lower id), the token's maximum value, and among
+// the lanes holding it the lowest id (a ballot; a second reduction only when several
+// lanes tie).  Lane j of the token keeps round j's id and logit; the k softmax
+// weights are formed after the rounds, one per lane.  The kernel is bound by its VALU
+// work: an exp and a division in every round cost a third of it (78 -> 60 us on the
+// learner batch), and two tokens per wave share every reduction's instructions.
+template <int NPL, int LPT>
 __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
+  constexpr int TPW = kWave / LPT;  // tokens per wave
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;  // uniform over the wave
+  const int sub = lane / LPT, ll = lane % LPT;
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  if (t0 >= a.T) return;  // uniform over the wave
+  const int64_t t = t0 + sub;
+  const bool valid = t < a.T;  // the second token of the last wave may not exist
   const int E = a.E;
   const float *lg = a.logits + t * E;
   float lv[NPL];
@@ -77,22 +88,22 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
   bool nan = false;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
+    const int e = ll + LPT * i;
     lv[i] = -INFINITY;
-    if (e < E) {
+    if (valid && e < E) {
       lv[i] = lg[e];
       nan |= lv[i] != lv[i];
       mx = fmaxf(mx, lv[i]);
     }
   }
-  mx = wave_max_dpp(mx);
+  mx = wave_max_dpp<LPT>(mx);
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) s += expf(lv[i] - mx);
+    const int e = ll + LPT * i;
+    if (valid && e < E) s += expf(lv[i] - mx);
   }
-  s = wave_sum_dpp(s);
+  s = wave_sum_dpp<LPT>(s);
   uint32_t taken = 0;
   int my_id = 0;
   float my_v = -INFINITY;
@@ -101,29 +112,41 @@ __global__ __launch_bounds__(256) void k_topk(PermuteArgs a) {
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
-      const int e = lane + kWave * i;
+      const int e = ll + LPT * i;
       // ids of one lane increase with i, so the first of equal values has the lowest id
       if (e < E && !((taken >> i) & 1u) && (lv[i] > bv || (bi == 0x7FFFFFFF && lv[i] == bv))) { bv = lv[i]; bi = e; }
     }
-    const float vmax = wave_max_dpp(bv);
+    const float vmax = wave_max_dpp<LPT>(bv);
     const uint64_t cand = __ballot(bi != 0x7FFFFFFF && bv == vmax);
     int wid;
-    if (cand == 0) {
-      wid = 0x7FFFFFFF;  // every remaining logit is NaN
-    } else if ((cand & (cand - 1)) == 0) {
-      wid = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(cand));
+    if (LPT == 64) {
+      if (cand == 0) {
+        wid = 0x7FFFFFFF;  // every remaining logit is NaN
+      } else if ((cand & (cand - 1)) == 0) {
+        wid = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(cand));
+      } else {
+        wid = wave_min_dpp(((cand >> lane) & 1) ? bi : 0x7FFFFFFF);
+      }
     } else {
-      wid = wave_min_dpp(((cand >> lane) & 1) ? bi : 0x7FFFFFFF);
+      // the two halves' candidate lanes: one each (the usual case) is read directly
+      const uint32_t c0 = (uint32_t)cand, c1 = (uint32_t)(cand >> 32);
+      if ((c0 & (c0 - 1)) == 0 && (c1 & (c1 - 1)) == 0) {
+        const int w0 = c0 ? __builtin_amdgcn_readlane(bi, (int)__builtin_ctz(c0)) : 0x7FFFFFFF;
+        const int w1 = c1 ? __builtin_amdgcn_readlane(bi, 32 + (int)__builtin_ctz(c1)) : 0x7FFFFFFF;
+        wid = sub ? w1 : w0;
+      } else {
+        wid = wave_min_dpp<LPT>(((cand >> lane) & 1) ? bi : 0x7FFFFFFF);
+      }
     }
-    if (wid < E && (wid & 63) == lane) taken |= 1u << (wid >> 6);
-    if (lane == j) { my_id = wid; my_v = vmax; }
+    if (wid < E && (wid % LPT) == ll) taken |= 1u << (wid / LPT);
+    if (ll == j) { my_id = wid; my_v = vmax; }
   }
   float my_w = 0.0f;
-  if (lane < a.k) my_w = expf(my_v - mx) / s;
-  if (a.flags & NV4_RENORM) my_w = my_w / wave_sum_dpp(my_w);  // lanes >= k hold 0
-  if (lane < a.k) {
-    a.topk_ids[t * a.k + lane] = my_id;
-    a.topk_w[t * a.k + lane] = my_w;
+  if (ll < a.k) my_w = expf(my_v - mx) / s;
+  if (a.flags & NV4_RENORM) my_w = my_w / wave_sum_dpp<LPT>(my_w);  // lanes >= k hold 0
+  if (valid && ll < a.k) {
+    a.topk_ids[t * a.k + ll] = my_id;
+    a.topk_w[t * a.k + ll] = my_w;
   }
   // any lane's NaN (each lane held only its own experts' logits)
   if (__ballot(nan) != 0 && lane == 0 && a.dev_status) atomicOr(a.dev_status, kDsNanLogit);
@@ -305,12 +328,13 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t stream) {
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   if (a.logits) {
-    const unsigned gt = (unsigned)((a.T + 3) / 4);
-    if (a.E <= 64) k_topk<1><<<gt, 256, 0, stream>>>(a);
-    else if (a.E <= 128) k_topk<2><<<gt, 256, 0, stream>>>(a);
-    else if (a.E <= 256) k_topk<4><<<gt, 256, 0, stream>>>(a);
-    else if (a.E <= 512) k_topk<8><<<gt, 256, 0, stream>>>(a);
-    else k_topk<16><<<gt, 256, 0, stream>>>(a);
+    // four waves per workgroup; two tokens per wave up to 128 experts (k <= 32 <= LPT)
+    const unsigned g1 = (unsigned)((a.T + 3) / 4), g2 = (unsigned)((a.T + 7) / 8);
+    if (a.E <= 64) k_topk<2, 32><<<g2, 256, 0, stream>>>(a);
+    else if (a.E <= 128) k_topk<4, 32><<<g2, 256, 0, stream>>>(a);
+    else if (a.E <= 256) k_topk<4, 64><<<g1, 256, 0, stream>>>(a);
+    else if (a.E <= 512) k_topk<8, 64><<<g1, 256, 0, stream>>>(a);
+    else k_topk<16, 64><<<g1, 256, 0, stream>>>(a);
   }
   k_rank<<<nchunks, 64, 0, stream>>>(a, nbits);
   k_scan_chunks<<<a.E, 64, 0, stream>>>(a, nchunks);

@@ -39,7 +39,8 @@ def test_route_and_permute_configs(gpu_lib, cfg_name):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (100, 1, 1), (33, 8, 8), (257, 300, 5), (64, 1024, 32), (5000, 64, 3)])
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (100, 1, 1), (33, 8, 8), (257, 300, 5), (64, 1024, 32), (5000, 64, 3),
+                                   (77, 128, 32), (31, 65, 4), (3, 128, 8)])
 def test_route_shapes(gpu_lib, T, E, k):
     lg = synth.rng(T + E + k).standard_normal((T, E)).astype(np.float32)
     lg[0, :] = 0.25  # full tie in one row: lowest ids
